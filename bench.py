@@ -1,0 +1,231 @@
+"""Benchmark of the prefill routed-expert product on one MI355X.
+
+One step = one layer's whole routed-expert product: quantize_scatter,
+expert_gate_up, swiglu_q8 and expert_down (four launches) over inputs already
+resident in HBM.  The plan (host counting sort + one upload) is built once
+outside the timed region and timed separately.
+
+Prints ONE JSON line: value = effective int8 TOPS of the 16,384-token layer
+(2 x useful MACs / time), ms_per_step = ms per layer; the 2k, 8k and t128
+layers are reported alongside, the roofline of the dominant kernel, and the
+oracle timed on a bounded sample of rows on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "ms/layer + effective int8 TOPS (512 experts, top-10) at 2K/8K/16K tokens"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+MFMA_I8_PEAK_TOPS = 5000.0      # dense int8 MFMA
+# fp32 FMA on the vector ALU without packed instructions:
+# 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz
+VALU_F32_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+KERNELS = ["quantize_scatter", "expert_gate_up", "swiglu_q8", "expert_down"]
+KERNEL_SOURCES = {
+    "expert_gate_up": "quantized_moe_expert_scatter_amd/csrc/expert_kernels.hip",
+    "expert_down": "quantized_moe_expert_scatter_amd/csrc/expert_kernels.hip",
+    "quantize_scatter": "quantized_moe_expert_scatter_amd/csrc/quant_kernels.hip",
+    "swiglu_q8": "quantized_moe_expert_scatter_amd/csrc/quant_kernels.hip",
+}
+
+
+def algorithmic(cfg, counts):
+    """Bytes and int8 ops each step moves / performs, counted once (weights of
+    touched experts only)."""
+    T, H, F, K = cfg.tokens, cfg.hidden, cfg.n_ff, cfg.topk
+    R = T * K
+    touched = int(np.count_nonzero(counts))
+    dn_blk = 64 if cfg.down_type == 1 else 32
+    w_gu = touched * 2 * F * (H // 64) * 18
+    w_dn = touched * H * (F // dn_blk) * 18
+    q8 = lambda n: n + n // 32 * 8
+    by = {
+        "quantize_scatter": T * H * 4 + R * q8(H),
+        "expert_gate_up": R * q8(H) + w_gu + R * 2 * F * 4,
+        "swiglu_q8": R * 2 * F * 4 + R * q8(F),
+        "expert_down": R * q8(F) + w_dn + R * H * 4,
+    }
+    ops = {"expert_gate_up": 2 * R * 2 * F * H, "expert_down": 2 * R * H * F}
+    # epilogue: two fp32 FMAs (4 flop) per (row, output, 32-value block)
+    alu = {"expert_gate_up": 4 * R * 2 * F * (H // 32), "expert_down": 4 * R * H * (F // 32)}
+    return by, ops, alu
+
+
+def time_layer(D, steps, warmup):
+    import torch
+    stream = torch.cuda.current_stream()
+    fns = [D.quantize_scatter, D.expert_gate_up, D.swiglu_q8, D.expert_down]
+    for _ in range(warmup):
+        D.run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(steps):
+        ev[s][0].record(stream)
+        for i, f in enumerate(fns):
+            f()
+            ev[s][i + 1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    per_kernel = {k: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]))
+                  for i, k in enumerate(KERNELS)}
+    return total_ms / steps, per_kernel
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb").read()
+    if rec.get("source_sha1") != hashlib.sha1(src).hexdigest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def run_cpu_baseline(L, threads, target_rows):
+    from oracle import oracle
+    cfg = L.cfg
+    pl = oracle.plan(L.ids, cfg.n_expert, 64)
+    row_e = pl.row_expert()
+    # all rows of the first experts, so every sampled expert's weights are
+    # decoded once for many rows, as in a whole layer
+    n_e = int(np.searchsorted(pl.offsets, target_rows))
+    n_e = max(1, min(n_e, cfg.n_expert))
+    rows = np.arange(0, int(pl.offsets[n_e]), dtype=np.int32)
+    t0 = time.perf_counter()
+    xq = oracle.quantize_scatter(L.x, cfg.topk, pl.perm, rows=rows)
+    gu = oracle.expert_product(L.w_gu.wtype, L.w_gu.buf, L.w_gu.offsets, cfg.n_expert,
+                               2 * cfg.n_ff, cfg.hidden, None, xq, row_e[rows], n_threads=threads)
+    hq = oracle.swiglu_q8(gu, cfg.n_ff)
+    oracle.expert_product(L.w_down.wtype, L.w_down.buf, L.w_down.offsets, cfg.n_expert,
+                          cfg.hidden, cfg.n_ff, L.w_down.codebook, hq, row_e[rows],
+                          n_threads=threads)
+    dt = time.perf_counter() - t0
+    ms_layer = dt * 1e3 * cfg.rows / rows.size
+    return {"value": round(ms_layer, 1), "unit": "ms/layer", "cores": threads, "kind": "oracle",
+            "sample": f"{rows.size} of {cfg.rows} expert-sorted rows (all rows of experts "
+                      f"0..{n_e - 1}) of the {cfg.name} layer, full chain, {dt:.1f} s wall, "
+                      f"scaled by rows"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="16k", choices=["tiny", "2k", "8k", "16k", "t128"])
+    ap.add_argument("--also", default="2k,8k,t128", help="other layers reported alongside")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=6000)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    from quantized_moe_expert_scatter_amd import workloads as wl
+    from quantized_moe_expert_scatter_amd.layer import DeviceLayer
+
+    assert torch.cuda.is_available(), "bench needs the GPU"
+    torch.cuda.set_device(0)
+    results = {}
+    main_cfg = wl.CONFIGS[args.workload]
+    names = [args.workload] + [n for n in args.also.split(",") if n and n != args.workload]
+    main_layer = None
+    for name in names:
+        cfg = wl.CONFIGS[name]
+        print(f"[bench] {name}: generating inputs", file=sys.stderr, flush=True)
+        L = wl.make_layer(cfg)
+        t0 = time.perf_counter()
+        D = DeviceLayer(L.x, L.ids, L.w_gu, L.w_down, chunk_rows=64)
+        torch.cuda.synchronize()
+        setup_s = time.perf_counter() - t0
+        counts = D.plan.query()[0]
+        steps = args.steps if name == args.workload else max(5, args.steps // 5)
+        ms, per_kernel = time_layer(D, steps, args.warmup)
+        by, ops, alu = algorithmic(cfg, counts)
+        useful_ops = ops["expert_gate_up"] + ops["expert_down"]
+        results[name] = {"ms_per_layer": round(ms, 4), "tops": round(useful_ops / (ms * 1e-3) / 1e12, 1),
+                         "per_kernel_ms": {k: round(v, 4) for k, v in per_kernel.items()},
+                         "algorithmic_bytes": int(sum(by.values())),
+                         "hbm_floor_ms": round(sum(by.values()) / (HBM_PEAK_GBS * 1e9) * 1e3, 4),
+                         "steps": steps, "setup_s": round(setup_s, 2)}
+        print(f"[bench] {name}: {ms:.3f} ms/layer {results[name]['tops']} TOPS {per_kernel}",
+              file=sys.stderr, flush=True)
+        if name == args.workload:
+            main_layer, main_by, main_ops, main_alu, main_pk = L, by, ops, alu, per_kernel
+        D.close()
+        del D
+        torch.cuda.empty_cache()
+
+    m = results[args.workload]
+    # roofline of the dominant kernel (the one with the largest share of the step)
+    dom = max(main_pk, key=main_pk.get)
+    t = main_pk[dom] * 1e-3
+    fr = {"hbm": (main_by[dom] / t / 1e9, HBM_PEAK_GBS, "GB/s")}
+    if dom in main_ops:
+        fr["mfma"] = (main_ops[dom] / t / 1e12, MFMA_I8_PEAK_TOPS, "TOPS")
+        fr["alu"] = (main_alu[dom] / t / 1e12, VALU_F32_PEAK_TFLOPS, "TFLOP/s")
+    bound = max(fr, key=lambda k: fr[k][0] / fr[k][1])
+    ach, peak, unit = fr[bound]
+    roof = {"kernel": dom, "bound": bound, "achieved": round(ach, 1), "peak": round(peak, 1),
+            "unit": unit, "frac": round(ach / peak, 3),
+            "traffic": traffic_for(dom, args.workload),
+            "algorithmic_bytes_per_launch": int(main_by[dom]),
+            "other_bounds": {k: {"achieved": round(v[0], 1), "peak": round(v[1], 1), "unit": v[2],
+                                 "frac": round(v[0] / v[1], 3)} for k, v in fr.items() if k != bound}}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = min(16, os.cpu_count() or 1)
+        print(f"[bench] cpu baseline on {threads} threads", file=sys.stderr, flush=True)
+        cpu = run_cpu_baseline(main_layer, threads, args.cpu_rows)
+
+    line = {
+        "metric": METRIC,
+        "value": m["tops"],
+        "unit": "effective int8 TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": m["ms_per_layer"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded: X ~ N(0,1), uniform Q2_0 codes, fp16 scales U[0.01,0.05])",
+        "config": {"workload": f"{main_cfg.name}: T={main_cfg.tokens}, hidden {main_cfg.hidden}, "
+                               f"n_ff {main_cfg.n_ff}, {main_cfg.n_expert} experts, top-{main_cfg.topk} "
+                               f"{main_cfg.routing}, gate/up Q2_0, down "
+                               f"{'Q2_0' if main_cfg.down_type == 1 else 'NL4'}",
+                   "tokens": main_cfg.tokens, "rows": main_cfg.rows, "chunk_rows": 64},
+        "per_kernel_ms": m["per_kernel_ms"],
+        "hbm_floor_ms": m["hbm_floor_ms"],
+        "layers": {k: {kk: v[kk] for kk in ("ms_per_layer", "tops", "per_kernel_ms", "hbm_floor_ms")}
+                   for k, v in results.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

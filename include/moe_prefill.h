@@ -1,0 +1,193 @@
+/*
+ * moe_prefill.h -- C ABI of the MI355X (gfx950) prefill routed-expert product.
+ *
+ * One MoE layer's routed experts over a prompt chunk of T tokens, in the
+ * steps the "Strata" pages describe (PR #3752 "GP100 weight-stationary
+ * experts": commit list and Approach; PR #2145 "fused int8 prompt experts on
+ * Turing": description):
+ *
+ *   moe_prefill_plan   routing ids -> expert-sorted rows, offsets, chunk table
+ *   quantize_scatter   X (fp32) -> q8_1 rows, one copy per (token, expert)
+ *   expert_gate_up     q8_1 rows x Q2_0 gate/up weights -> GU (fp32)
+ *   swiglu_q8          GU -> q8_1 of silu(gate) * up, H never stored as floats
+ *   expert_down        q8_1 H rows x down weights -> one fp32 row per (token, expert)
+ *
+ * Conventions shared by every entry point:
+ *   - Device pointers are HIP device addresses on the current device; host
+ *     pointers are ordinary process memory.  `stream` is a hipStream_t (NULL
+ *     is the null stream).  Work is enqueued asynchronously on `stream`.
+ *   - The caller owns every device buffer (inputs, outputs, weights, the plan
+ *     workspace).  The library never allocates device memory.  The moe_plan
+ *     object is a host object owned by the library until moe_plan_destroy.
+ *   - Every call validates its arguments on the host before it enqueues
+ *     anything; on error it returns a negative moe_status and launches
+ *     nothing.  A step over a plan with no rows (tokens == 0) does nothing
+ *     and accepts NULL buffers.  Launch failures reported by HIP return MOE_EHIP.  No call
+ *     throws across the ABI.
+ *   - Results are deterministic: no floating-point atomics, every output
+ *     element is written by exactly one thread with a fixed operation order.
+ *
+ * Data formats (the byte layouts are this project's own; the pages name the
+ * formats but do not print their bits):
+ *   q8_1 row of C values (C % 32 == 0), moe_q8_1_bytes(1, C) = 1.25*C bytes:
+ *       int8 q[C] | fp32 d[C/32] | int32 s[C/32]
+ *     block b holds values 32b..32b+31 with d = max|x|/127 (fp32 divide),
+ *     q = x/d rounded half away from zero and clamped to [-127, 127],
+ *     s = sum of the block's q; a block with d == 0 is all zeros.
+ *   Q2_0 matrix [rows x cols] (cols % 64 == 0), rows*cols/64*18 bytes:
+ *       codes plane: rows*cols/64 blocks of 16 bytes, row-major (row, block);
+ *         value 16*j+b of a block is bits 2j..2j+1 of byte b; weight = d*(code-2)
+ *       scales plane: rows*cols/64 binary16 d, same order, right after the codes.
+ *   NL4 matrix [rows x cols] (cols % 32 == 0), rows*cols/32*18 bytes:
+ *       codes plane: 16-byte blocks of 32 values, value b in the low nibble of
+ *         byte b, value 16+b in the high nibble; weight = d*codebook[code]
+ *       scales plane: binary16 d per 32-value block.
+ *   Expert outputs are fp32.  The per-32-value epilogue is, for each output,
+ *       acc = 0; for each 32-value block b in K order:
+ *         acc = fmaf(dx_b, dw_b * (float)dot_b, acc)
+ *     where dot_b is the exact int32 dot of the block's q with the weight's
+ *     integer codes (Q2_0: code-2; NL4: codebook entry) and dw_b the block's
+ *     weight scale (a Q2_0 block's two 32-value halves share it).
+ */
+#ifndef MOE_PREFILL_H
+#define MOE_PREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,   /* null pointer, non-positive or inconsistent size, id out of range */
+    MOE_EALIGN = -2,   /* a pointer or offset is not 16-byte aligned */
+    MOE_EFORMAT = -3,  /* unknown weight type, or dims not a multiple of the block */
+    MOE_ESIZE = -4,    /* a caller buffer is smaller than the size query demands */
+    MOE_EHIP = -5,     /* HIP reported an error while enqueueing */
+    MOE_ESTATE = -6    /* the plan was built without a device workspace */
+} moe_status;
+
+typedef enum { MOE_W_Q2_0 = 1, MOE_W_NL4 = 2 } moe_wtype;
+
+/* The weights of one product (gate/up or down) for all experts of a layer,
+ * read in place: expert e's matrix starts at base + offset[e] ("Strata"
+ * PR #3752, commit list: a per-layer offset table from the expert cache's
+ * base, uploaded with the group bounds).
+ *   type      MOE_W_Q2_0, or MOE_W_NL4 (down product only)
+ *   rows      output features (gate/up: 2*n_ff; down: hidden), % 64 == 0
+ *   cols      contraction length (gate/up: hidden; down: n_ff), % 64 (Q2_0)
+ *             or % 32 (NL4) == 0
+ *   n_expert  number of experts
+ *   base      device pointer, 16-byte aligned
+ *   base_bytes size of the buffer at base (every expert must lie inside it)
+ *   offset    host pointer [n_expert]: byte offsets, each 16-byte aligned
+ *   codebook  host pointer [16] int8, NL4 only (NULL for Q2_0)
+ * The descriptor is copied by moe_prefill_plan; the weight bytes themselves
+ * must stay valid and unchanged while the plan is used. */
+typedef struct {
+    int type;
+    int rows;
+    int cols;
+    int n_expert;
+    const void *base;
+    size_t base_bytes;
+    const uint64_t *offset;
+    const int8_t *codebook;
+} moe_weights;
+
+typedef struct moe_plan moe_plan;  /* opaque host object */
+
+/* Bytes of `rows` q8_1 rows of `cols` values: rows * 1.25 * cols.
+ * Returns 0 if cols % 32 != 0 or a size is negative. */
+size_t moe_q8_1_bytes(int rows, int cols);
+
+/* Bytes of one expert's matrix in the given format (0 on a bad format/dim). */
+size_t moe_weight_bytes(int type, int rows, int cols);
+
+/* Device workspace the plan needs for T tokens, top-k, n_expert experts and
+ * chunks of at most chunk_rows rows (sorted-row maps, expert offsets, the
+ * chunk table, the per-product work lists and both weight offset tables).
+ * Returns 0 on invalid sizes. */
+size_t moe_plan_device_bytes(int tokens, int topk, int n_expert, int chunk_rows);
+
+/* Build a layer's plan ("Strata" PR #3752: quantize_scatter sorts each
+ * expert's rows together; the CTAs take row chunks of the experts, largest
+ * expert first; every expert at its own row count, no padding).
+ *   ids_host   host int32 [tokens*topk], ids_host[t*topk+k] = k-th expert of
+ *              token t, each in [0, n_expert).  A token may name an expert
+ *              twice; that gives two rows.
+ *   chunk_rows 1..64: rows per chunk (64 is the pages' choice).
+ *   w_gu       gate/up weights: Q2_0, rows = 2*n_ff, cols = hidden.
+ *   w_down     down weights: Q2_0 or NL4, rows = hidden, cols = n_ff.
+ *   plan_dev   device workspace of moe_plan_device_bytes(...) bytes, 16-byte
+ *              aligned, owned by the caller, not touched by anything else
+ *              while the plan lives; NULL builds a host-only plan (for
+ *              inspection: the kernels refuse it with MOE_ESTATE).
+ *   stream     the plan is uploaded with one asynchronous host-to-device
+ *              copy on this stream; later launches on the same stream see it.
+ * Sorted rows: expert e owns rows [off[e], off[e+1]); inside an expert the
+ * rows keep ascending t*topk+k order.  Chunks are (expert, first row, rows),
+ * experts by descending row count, ties by ascending expert id.
+ * On success *out receives the plan; on error *out is left NULL. */
+int moe_prefill_plan(const int32_t *ids_host, int tokens, int topk, int n_expert,
+                     int chunk_rows, const moe_weights *w_gu, const moe_weights *w_down,
+                     void *plan_dev, size_t plan_dev_bytes, void *stream, moe_plan **out);
+
+/* Host view of a plan, for inspection and tests: any pointer may be NULL.
+ * counts [n_expert], offsets [n_expert+1], perm [tokens*topk] (sorted row ->
+ * t*topk+k), chunks [4*n_chunks] (expert, first row, rows, 0). */
+int moe_plan_query(const moe_plan *plan, int *rows, int *n_chunks,
+                   int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *chunks);
+
+/* Release the plan (waits for its upload to finish; does not free plan_dev). */
+void moe_plan_destroy(moe_plan *plan);
+
+/* Step 1 ("Strata" PR #3752, commit list: quantize_scatter).  Quantize each
+ * token's row of x to q8_1 and write it to each of its topk expert-sorted
+ * rows.  x: device fp32 [tokens x hidden] row-major, 16-byte aligned.
+ * xq: device, moe_q8_1_bytes(tokens*topk, hidden) bytes, 16-byte aligned. */
+int quantize_scatter(const moe_plan *plan, const float *x, void *xq, void *stream);
+
+/* Step 2 ("Strata" PR #3752: gate/up as one launch over all experts;
+ * PR #2145: exact int32 block sums, per-32-value fp32 epilogue).
+ * gu[r][n] for every sorted row r and n < 2*n_ff: the epilogue above over the
+ * q8_1 row r of xq and row n of its expert's gate/up matrix.  Gate is
+ * n < n_ff, up is n >= n_ff.
+ * xq: device q8_1 rows [tokens*topk x hidden]; gu: device fp32
+ * [tokens*topk x 2*n_ff] in sorted-row order, 16-byte aligned. */
+int expert_gate_up(const moe_plan *plan, const void *xq, float *gu, void *stream);
+
+/* Step 3 ("Strata" PR #3752, swiglu_quant commit: swiglu and the q8_1 rows
+ * the down product reads, in one pass, H never stored).  For each sorted row
+ * and j < n_ff: h_j = silu(g_j) * u_j with g_j = gu[r][j], u_j = gu[r][n_ff+j]
+ * and silu(g) = g / (1 + E) in fp32, E = e^-g rounded to the nearest binary32
+ * (through a binary64 exponential); hq row r = q8_1 of h.
+ * gu: device fp32 [tokens*topk x 2*n_ff]; hq: device
+ * moe_q8_1_bytes(tokens*topk, n_ff) bytes; both 16-byte aligned. */
+int swiglu_q8(const moe_plan *plan, const float *gu, void *hq, void *stream);
+
+/* Step 4 ("Strata" PR #3752: the down product as one launch into one row per
+ * (token, expert), the K loop stopping at n_ff).
+ * dm[t*topk+k][n] for n < hidden: the epilogue over sorted row r (whose
+ * perm[r] = t*topk+k) of hq and row n of the expert's down matrix.
+ * hq: device q8_1 rows [tokens*topk x n_ff]; dm: device fp32
+ * [tokens*topk x hidden], 16-byte aligned. */
+int expert_down(const moe_plan *plan, const void *hq, float *dm, void *stream);
+
+/* Test export: the exact int32 dots of every (sorted row, output, 32-value
+ * block) of one product, computed by the same kernel path as the product.
+ * product 0 = gate/up (act = xq), 1 = down (act = hq).  Rows
+ * [row_begin, row_begin+n_rows) of the sorted order; dots: device int32
+ * [n_rows x out_rows x cols/32], 16-byte aligned. */
+int moe_debug_block_dots(const moe_plan *plan, int product, const void *act,
+                         int row_begin, int n_rows, int32_t *dots, void *stream);
+
+/* Text of a status code (static storage). */
+const char *moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_PREFILL_H */

@@ -261,10 +261,14 @@ int orc_block_dots(int wtype, const uint8_t *w_base, const uint64_t *w_off,
  * "Strata" PR #3752, swiglu_quant commit: swiglu of the gate/up row, then
  * q8_1 of each 32-value block of the result, in one pass, H never stored.
  * The expression is not printed; our reading is silu(g) * u with
- * silu(g) = g / (1 + exp(-g)), in fp32. */
+ * silu(g) = g / (1 + e^-g) in fp32, where e^-g is the binary32 value
+ * nearest to the exact exponential (computed in binary64 and rounded once;
+ * a double rounding can only differ when e^-g lies within about 2^-29 of a
+ * binary32 rounding boundary). */
 float orc_swiglu(float g, float u)
 {
-    const float silu = g / (1.0f + expf(-g));
+    const float e = (float)exp(-(double)g);
+    const float silu = g / (1.0f + e);
     return silu * u;
 }
 

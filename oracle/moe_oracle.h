@@ -86,7 +86,8 @@ int orc_block_dots(int wtype, const uint8_t *w_base, const uint64_t *w_off,
                    const uint8_t *act, const int32_t *act_expert, int n_act,
                    int32_t *dots);
 
-/* SwiGLU of one value pair: silu(g) * u with silu(g) = g / (1 + expf(-g)). */
+/* SwiGLU of one value pair: silu(g) * u with silu(g) = g / (1 + E) in fp32,
+ * E = e^-g rounded to the nearest binary32 (via binary64). */
 float orc_swiglu(float g, float u);
 
 /* swiglu + q8_1 of `rows` gate/up rows: gu row = [gate F | up F] (split

@@ -1,0 +1,76 @@
+// internal.h -- shared between the host boundary (moe_prefill.cpp) and the
+// HIP kernels: the device plan layout and the launcher entry points.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace moe {
+
+constexpr int kXcds = 8;           // MI355X: 8 accelerator dies, each with its own L2
+constexpr int kMaxChunkRows = 64;  // rows of one chunk = two 32-row MFMA tiles
+constexpr int kTileRows = 256;     // weight rows (outputs) per workgroup: 4 waves x 64
+constexpr uint32_t kMagicBits = 0x4B400000u;  // 1.5 * 2^23 as binary32
+
+constexpr size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
+
+inline int max_chunks(int rows, int n_expert, int chunk_rows) {
+    return rows / chunk_rows + n_expert + 1;
+}
+
+// Byte offsets of the sections of the device plan workspace.  Every section
+// is 16-byte aligned.
+struct PlanLayout {
+    size_t perm;     // int32 [R]     sorted row -> t*K+k
+    size_t inv;      // int32 [R]     t*K+k -> sorted row
+    size_t chunks;   // int32 [maxc][4] chunk table grouped by XCD (see xcd)
+    size_t xcd;      // int32 [2*kXcds]: first chunk and chunk count of each XCD list
+    size_t gu_off;   // uint64 [E]    gate/up expert byte offsets
+    size_t dn_off;   // uint64 [E]    down expert byte offsets
+    size_t total;
+};
+
+inline PlanLayout plan_layout(int tokens, int topk, int n_expert, int chunk_rows) {
+    PlanLayout L{};
+    const size_t R = size_t(tokens) * size_t(topk);
+    size_t o = 0;
+    L.perm = o;   o += align16(R * 4);
+    L.inv = o;    o += align16(R * 4);
+    L.chunks = o; o += align16(size_t(max_chunks(int(R), n_expert, chunk_rows)) * 16);
+    L.xcd = o;    o += align16(size_t(2 * kXcds) * 4);
+    L.gu_off = o; o += align16(size_t(n_expert) * 8);
+    L.dn_off = o; o += align16(size_t(n_expert) * 8);
+    L.total = o;
+    return L;
+}
+
+// Arguments of one expert product launch (gate/up or down).
+struct ProductArgs {
+    const uint8_t *act;        // q8_1 rows in sorted order
+    const uint8_t *w_base;     // weight buffer
+    const uint64_t *w_off;     // device: expert byte offsets
+    const int32_t *chunks;     // device: XCD-grouped chunk table
+    const int32_t *xcd;        // device: per-XCD list starts and counts
+    const int32_t *perm;       // device: sorted row -> output row (NULL: identity)
+    float *out;                // fp32 outputs
+    int32_t *dots;             // debug: int32 block dots instead of outputs
+    int wtype;                 // 1 Q2_0, 2 NL4
+    int cols;                  // contraction length
+    int out_rows;              // weight rows of one expert = output columns
+    int n_tiles;               // ceil(out_rows / kTileRows)
+    int max_items;             // items per XCD list (grid = kXcds * max_items)
+    int dots_row_begin;
+    int dots_n_rows;
+    int8_t codebook[16];
+};
+
+// Launchers (defined in the .hip files).  Return hipSuccess or the launch error.
+hipError_t launch_quantize_scatter(const float *x, int tokens, int hidden, int topk,
+                                   const int32_t *inv, uint8_t *xq, hipStream_t stream);
+hipError_t launch_swiglu_q8(const float *gu, int rows, int n_ff, uint8_t *hq,
+                            hipStream_t stream);
+hipError_t launch_expert_product(const ProductArgs &args, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,330 @@
+// moe_prefill.cpp -- host side of the C ABI: argument validation, the plan
+// (counting sort, chunk table, XCD work lists), its upload, and the launches.
+//
+// "Strata" PR #3752 (commit list, Approach): the experts' rows are made
+// contiguous by quantize_scatter, the layer's expert offsets and the CTAs'
+// chunk table go up to the device together with the group bounds, and each
+// product runs as one launch over all experts, chunks taken largest expert
+// first, each expert at its own row count.
+#include "../../include/moe_prefill.h"
+#include "internal.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <vector>
+
+using namespace moe;
+
+struct moe_plan {
+    int tokens = 0, topk = 0, n_expert = 0, chunk_rows = 0, rows = 0;
+    int hidden = 0, n_ff = 0;
+    moe_weights gu{}, dn{};
+    std::vector<uint64_t> gu_off, dn_off;
+    int8_t dn_codebook[16] = {};
+    std::vector<int32_t> counts, offsets, perm, inv, chunks, dev_chunks;
+    int32_t xcd_tab[2 * kXcds] = {};
+    int n_chunks = 0;
+    int max_xcd_chunks = 0;
+    void *plan_dev = nullptr;
+    PlanLayout layout{};
+    void *staging = nullptr;
+    hipEvent_t uploaded = nullptr;
+};
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int block_values(int type) { return type == MOE_W_Q2_0 ? 64 : (type == MOE_W_NL4 ? 32 : 0); }
+
+size_t weight_bytes(int type, int rows, int cols) {
+    const int blk = block_values(type);
+    if (blk == 0 || rows <= 0 || cols <= 0 || cols % blk) return 0;
+    return size_t(rows) * size_t(cols / blk) * 18u;
+}
+
+int check_weights(const moe_weights *w, int n_expert, bool allow_nl4) {
+    if (!w || !w->base || !w->offset) return MOE_EINVAL;
+    if (w->type != MOE_W_Q2_0 && !(allow_nl4 && w->type == MOE_W_NL4)) return MOE_EFORMAT;
+    if (w->n_expert != n_expert || w->rows <= 0 || w->cols <= 0) return MOE_EINVAL;
+    if (w->rows % 64 || w->cols % block_values(w->type)) return MOE_EFORMAT;
+    if (w->type == MOE_W_NL4 && !w->codebook) return MOE_EINVAL;
+    if (!aligned16(w->base)) return MOE_EALIGN;
+    const size_t per = weight_bytes(w->type, w->rows, w->cols);
+    for (int e = 0; e < n_expert; ++e) {
+        if (w->offset[e] & 15u) return MOE_EALIGN;
+        if (w->offset[e] > w->base_bytes || w->base_bytes - w->offset[e] < per) return MOE_ESIZE;
+    }
+    return MOE_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_q8_1_bytes(int rows, int cols) {
+    if (rows < 0 || cols <= 0 || cols % 32) return 0;
+    return size_t(rows) * (size_t(cols) + size_t(cols) / 32 * 8);
+}
+
+size_t moe_weight_bytes(int type, int rows, int cols) { return weight_bytes(type, rows, cols); }
+
+size_t moe_plan_device_bytes(int tokens, int topk, int n_expert, int chunk_rows) {
+    if (tokens < 0 || topk <= 0 || n_expert <= 0 || chunk_rows <= 0 || chunk_rows > kMaxChunkRows)
+        return 0;
+    return plan_layout(tokens, topk, n_expert, chunk_rows).total;
+}
+
+const char *moe_status_string(int s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_EINVAL: return "invalid argument";
+        case MOE_EALIGN: return "pointer or offset not 16-byte aligned";
+        case MOE_EFORMAT: return "unsupported weight format or dimension";
+        case MOE_ESIZE: return "buffer too small";
+        case MOE_EHIP: return "HIP error";
+        case MOE_ESTATE: return "plan has no device workspace";
+        default: return "unknown status";
+    }
+}
+
+int moe_prefill_plan(const int32_t *ids, int tokens, int topk, int n_expert, int chunk_rows,
+                     const moe_weights *w_gu, const moe_weights *w_down, void *plan_dev,
+                     size_t plan_dev_bytes, void *stream, moe_plan **out) {
+    if (!out) return MOE_EINVAL;
+    *out = nullptr;
+    if (tokens < 0 || topk <= 0 || n_expert <= 0 || chunk_rows <= 0 || chunk_rows > kMaxChunkRows)
+        return MOE_EINVAL;
+    if (tokens > 0 && !ids) return MOE_EINVAL;
+    const long long R64 = (long long)tokens * topk;
+    if (R64 > (1LL << 30)) return MOE_EINVAL;
+    int st = check_weights(w_gu, n_expert, false);
+    if (st) return st;
+    st = check_weights(w_down, n_expert, true);
+    if (st) return st;
+    if (w_gu->rows % 2 || w_down->rows != w_gu->cols || w_down->cols * 2 != w_gu->rows)
+        return MOE_EINVAL;
+    const int R = int(R64);
+    for (int i = 0; i < R; ++i)
+        if (ids[i] < 0 || ids[i] >= n_expert) return MOE_EINVAL;
+    const PlanLayout L = plan_layout(tokens, topk, n_expert, chunk_rows);
+    if (plan_dev) {
+        if (!aligned16(plan_dev)) return MOE_EALIGN;
+        if (plan_dev_bytes < L.total) return MOE_ESIZE;
+    }
+
+    moe_plan *p = new (std::nothrow) moe_plan;
+    if (!p) return MOE_EINVAL;
+    p->tokens = tokens; p->topk = topk; p->n_expert = n_expert; p->chunk_rows = chunk_rows;
+    p->rows = R; p->hidden = w_gu->cols; p->n_ff = w_gu->rows / 2;
+    p->gu = *w_gu; p->dn = *w_down;
+    p->gu_off.assign(w_gu->offset, w_gu->offset + n_expert);
+    p->dn_off.assign(w_down->offset, w_down->offset + n_expert);
+    if (w_down->type == MOE_W_NL4) std::memcpy(p->dn_codebook, w_down->codebook, 16);
+    p->gu.offset = p->gu_off.data();
+    p->dn.offset = p->dn_off.data();
+    p->dn.codebook = p->dn_codebook;
+    p->layout = L;
+
+    // counting sort by expert, stable in t*K+k
+    p->counts.assign(n_expert, 0);
+    for (int i = 0; i < R; ++i) p->counts[ids[i]] += 1;
+    p->offsets.assign(n_expert + 1, 0);
+    for (int e = 0; e < n_expert; ++e) p->offsets[e + 1] = p->offsets[e] + p->counts[e];
+    p->perm.assign(R, 0);
+    p->inv.assign(R, 0);
+    {
+        std::vector<int32_t> fill(p->offsets.begin(), p->offsets.end() - 1);
+        for (int i = 0; i < R; ++i) {
+            const int r = fill[ids[i]]++;
+            p->perm[r] = i;
+            p->inv[i] = r;
+        }
+    }
+
+    // experts largest first (ties: lower id first), then their chunks
+    std::vector<int> order(n_expert);
+    for (int e = 0; e < n_expert; ++e) order[e] = e;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int a, int b) { return p->counts[a] > p->counts[b]; });
+    for (int e : order)
+        for (int r0 = 0; r0 < p->counts[e]; r0 += chunk_rows) {
+            const int nr = std::min(chunk_rows, p->counts[e] - r0);
+            p->chunks.insert(p->chunks.end(), {e, p->offsets[e] + r0, nr, 0});
+        }
+    p->n_chunks = int(p->chunks.size() / 4);
+
+    // XCD work lists: every chunk of an expert goes to one XCD so that its
+    // weights and activation rows are re-read from that XCD's L2; experts are
+    // dealt largest first to the XCD with the fewest rows so far.
+    {
+        std::vector<std::vector<int32_t>> lists(kXcds);
+        long long load[kXcds] = {};
+        for (int e : order) {
+            if (p->counts[e] == 0) continue;
+            int x = 0;
+            for (int k = 1; k < kXcds; ++k)
+                if (load[k] < load[x]) x = k;
+            load[x] += p->counts[e];
+            for (int r0 = 0; r0 < p->counts[e]; r0 += chunk_rows) {
+                const int nr = std::min(chunk_rows, p->counts[e] - r0);
+                lists[x].insert(lists[x].end(), {e, p->offsets[e] + r0, nr, 0});
+            }
+        }
+        int start = 0;
+        for (int x = 0; x < kXcds; ++x) {
+            const int cnt = int(lists[x].size() / 4);
+            p->xcd_tab[x] = start;
+            p->xcd_tab[kXcds + x] = cnt;
+            start += cnt;
+            p->max_xcd_chunks = std::max(p->max_xcd_chunks, cnt);
+            p->dev_chunks.insert(p->dev_chunks.end(), lists[x].begin(), lists[x].end());
+        }
+    }
+
+    if (plan_dev) {
+        p->plan_dev = plan_dev;
+        if (hipHostMalloc(&p->staging, L.total, hipHostMallocDefault) != hipSuccess) {
+            p->staging = nullptr;
+            moe_plan_destroy(p);
+            return MOE_EHIP;
+        }
+        uint8_t *s = static_cast<uint8_t *>(p->staging);
+        std::memset(s, 0, L.total);
+        std::memcpy(s + L.perm, p->perm.data(), size_t(R) * 4);
+        std::memcpy(s + L.inv, p->inv.data(), size_t(R) * 4);
+        std::memcpy(s + L.chunks, p->dev_chunks.data(), p->dev_chunks.size() * 4);
+        std::memcpy(s + L.xcd, p->xcd_tab, sizeof(p->xcd_tab));
+        std::memcpy(s + L.gu_off, p->gu_off.data(), size_t(n_expert) * 8);
+        std::memcpy(s + L.dn_off, p->dn_off.data(), size_t(n_expert) * 8);
+        hipStream_t hs = static_cast<hipStream_t>(stream);
+        if (hipEventCreateWithFlags(&p->uploaded, hipEventDisableTiming) != hipSuccess) {
+            p->uploaded = nullptr;
+            moe_plan_destroy(p);
+            return MOE_EHIP;
+        }
+        if (hipMemcpyAsync(plan_dev, s, L.total, hipMemcpyHostToDevice, hs) != hipSuccess ||
+            hipEventRecord(p->uploaded, hs) != hipSuccess) {
+            moe_plan_destroy(p);
+            return MOE_EHIP;
+        }
+    }
+    *out = p;
+    return MOE_OK;
+}
+
+int moe_plan_query(const moe_plan *p, int *rows, int *n_chunks, int32_t *counts, int32_t *offsets,
+                   int32_t *perm, int32_t *chunks) {
+    if (!p) return MOE_EINVAL;
+    if (rows) *rows = p->rows;
+    if (n_chunks) *n_chunks = p->n_chunks;
+    if (counts) std::copy(p->counts.begin(), p->counts.end(), counts);
+    if (offsets) std::copy(p->offsets.begin(), p->offsets.end(), offsets);
+    if (perm) std::copy(p->perm.begin(), p->perm.end(), perm);
+    if (chunks) std::copy(p->chunks.begin(), p->chunks.end(), chunks);
+    return MOE_OK;
+}
+
+void moe_plan_destroy(moe_plan *p) {
+    if (!p) return;
+    if (p->uploaded) {
+        (void)hipEventSynchronize(p->uploaded);
+        (void)hipEventDestroy(p->uploaded);
+    }
+    if (p->staging) (void)hipHostFree(p->staging);
+    delete p;
+}
+
+static const uint8_t *dev_at(const moe_plan *p, size_t off) {
+    return static_cast<const uint8_t *>(p->plan_dev) + off;
+}
+
+static int ready(const moe_plan *p) {
+    if (!p) return MOE_EINVAL;
+    if (!p->plan_dev) return MOE_ESTATE;
+    return MOE_OK;
+}
+
+int quantize_scatter(const moe_plan *p, const float *x, void *xq, void *stream) {
+    int st = ready(p);
+    if (st) return st;
+    if (p->rows == 0) return MOE_OK;
+    if (!x || !xq) return MOE_EINVAL;
+    if (!aligned16(x) || !aligned16(xq)) return MOE_EALIGN;
+    return hip_status(launch_quantize_scatter(
+        x, p->tokens, p->hidden, p->topk, reinterpret_cast<const int32_t *>(dev_at(p, p->layout.inv)),
+        static_cast<uint8_t *>(xq), static_cast<hipStream_t>(stream)));
+}
+
+static ProductArgs product_args(const moe_plan *p, int product, const void *act) {
+    ProductArgs a{};
+    const moe_weights &w = product == 0 ? p->gu : p->dn;
+    a.act = static_cast<const uint8_t *>(act);
+    a.w_base = static_cast<const uint8_t *>(w.base);
+    a.w_off = reinterpret_cast<const uint64_t *>(dev_at(p, product == 0 ? p->layout.gu_off
+                                                                          : p->layout.dn_off));
+    a.chunks = reinterpret_cast<const int32_t *>(dev_at(p, p->layout.chunks));
+    a.xcd = reinterpret_cast<const int32_t *>(dev_at(p, p->layout.xcd));
+    a.perm = product == 0 ? nullptr : reinterpret_cast<const int32_t *>(dev_at(p, p->layout.perm));
+    a.wtype = w.type;
+    a.cols = w.cols;
+    a.out_rows = w.rows;
+    a.n_tiles = (w.rows + kTileRows - 1) / kTileRows;
+    a.max_items = p->max_xcd_chunks * a.n_tiles;
+    if (w.type == MOE_W_NL4) std::memcpy(a.codebook, p->dn_codebook, 16);
+    return a;
+}
+
+int expert_gate_up(const moe_plan *p, const void *xq, float *gu, void *stream) {
+    int st = ready(p);
+    if (st) return st;
+    if (p->rows == 0) return MOE_OK;
+    if (!xq || !gu) return MOE_EINVAL;
+    if (!aligned16(xq) || !aligned16(gu)) return MOE_EALIGN;
+    ProductArgs a = product_args(p, 0, xq);
+    a.out = gu;
+    return hip_status(launch_expert_product(a, static_cast<hipStream_t>(stream)));
+}
+
+int swiglu_q8(const moe_plan *p, const float *gu, void *hq, void *stream) {
+    int st = ready(p);
+    if (st) return st;
+    if (p->rows == 0) return MOE_OK;
+    if (!gu || !hq) return MOE_EINVAL;
+    if (!aligned16(gu) || !aligned16(hq)) return MOE_EALIGN;
+    return hip_status(launch_swiglu_q8(gu, p->rows, p->n_ff, static_cast<uint8_t *>(hq),
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int expert_down(const moe_plan *p, const void *hq, float *dm, void *stream) {
+    int st = ready(p);
+    if (st) return st;
+    if (p->rows == 0) return MOE_OK;
+    if (!hq || !dm) return MOE_EINVAL;
+    if (!aligned16(hq) || !aligned16(dm)) return MOE_EALIGN;
+    ProductArgs a = product_args(p, 1, hq);
+    a.out = dm;
+    return hip_status(launch_expert_product(a, static_cast<hipStream_t>(stream)));
+}
+
+int moe_debug_block_dots(const moe_plan *p, int product, const void *act, int row_begin,
+                         int n_rows, int32_t *dots, void *stream) {
+    int st = ready(p);
+    if (st) return st;
+    if (!act || !dots || (product != 0 && product != 1)) return MOE_EINVAL;
+    if (row_begin < 0 || n_rows < 0 || (long long)row_begin + n_rows > p->rows) return MOE_EINVAL;
+    if (!aligned16(act) || !aligned16(dots)) return MOE_EALIGN;
+    if (n_rows == 0) return MOE_OK;
+    ProductArgs a = product_args(p, product, act);
+    a.dots = dots;
+    a.dots_row_begin = row_begin;
+    a.dots_n_rows = n_rows;
+    return hip_status(launch_expert_product(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

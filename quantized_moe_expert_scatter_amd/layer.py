@@ -1,0 +1,93 @@
+"""One MoE layer's routed-expert product on the device: buffers + the four steps.
+
+Plumbing only: torch provides device memory and the stream, the C ABI does
+every step of the computation.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import _lib
+from .workloads import ExpertWeights
+
+
+def _to_device(a: np.ndarray, device):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+class DeviceLayer:
+    """Uploads one layer's weights and inputs, owns every buffer of the path.
+
+    x: float32 [T, hidden]; ids: int32 [T, topk]; w_gu / w_down: ExpertWeights.
+    Buffers: xq (q8_1 rows of hidden), gu (fp32 [R, 2*n_ff]), hq (q8_1 rows of
+    n_ff), dm (fp32 [T*topk, hidden]); R = T*topk.
+    """
+
+    def __init__(self, x: np.ndarray, ids: np.ndarray, w_gu: ExpertWeights, w_down: ExpertWeights,
+                 chunk_rows: int = 64, device="cuda", stream=None):
+        import torch
+        self.device = torch.device(device)
+        self.tokens, self.hidden = x.shape
+        self.topk = ids.shape[1]
+        self.n_expert = w_gu.n_expert
+        self.n_ff = w_gu.rows // 2
+        self.rows = self.tokens * self.topk
+        self.chunk_rows = chunk_rows
+        self.x = _to_device(x.astype(np.float32, copy=False), self.device)
+        self.w_gu_dev = _to_device(w_gu.buf, self.device)
+        self.w_dn_dev = _to_device(w_down.buf, self.device)
+        self.w_gu = _lib.Weights(w_gu.wtype, w_gu.rows, w_gu.cols, w_gu.n_expert, self.w_gu_dev,
+                                 w_gu.buf.nbytes, w_gu.offsets)
+        self.w_dn = _lib.Weights(w_down.wtype, w_down.rows, w_down.cols, w_down.n_expert,
+                                 self.w_dn_dev, w_down.buf.nbytes, w_down.offsets, w_down.codebook)
+        u8 = torch.uint8
+        ws = _lib.moe_plan_device_bytes(self.tokens, self.topk, self.n_expert, chunk_rows)
+        self.workspace = torch.empty(max(ws, 16), dtype=u8, device=self.device)
+        self.xq = torch.empty(max(_lib.moe_q8_1_bytes(self.rows, self.hidden), 16), dtype=u8,
+                              device=self.device)
+        self.gu = torch.empty((max(self.rows, 1), 2 * self.n_ff), dtype=torch.float32,
+                              device=self.device)
+        self.hq = torch.empty(max(_lib.moe_q8_1_bytes(self.rows, self.n_ff), 16), dtype=u8,
+                              device=self.device)
+        self.dm = torch.empty((max(self.rows, 1), self.hidden), dtype=torch.float32,
+                              device=self.device)
+        self.plan = _lib.moe_prefill_plan(ids, self.n_expert, chunk_rows, self.w_gu, self.w_dn,
+                                          workspace=self.workspace, stream=stream)
+
+    # the four steps, each one kernel launch
+    def quantize_scatter(self, stream=None):
+        _lib.quantize_scatter(self.plan, self.x, self.xq, stream)
+
+    def expert_gate_up(self, stream=None):
+        _lib.expert_gate_up(self.plan, self.xq, self.gu, stream)
+
+    def swiglu_q8(self, stream=None):
+        _lib.swiglu_q8(self.plan, self.gu, self.hq, stream)
+
+    def expert_down(self, stream=None):
+        _lib.expert_down(self.plan, self.hq, self.dm, stream)
+
+    def run(self, stream=None):
+        self.quantize_scatter(stream)
+        self.expert_gate_up(stream)
+        self.swiglu_q8(stream)
+        self.expert_down(stream)
+
+    # host copies
+    def xq_host(self) -> np.ndarray:
+        rb = self.hidden + self.hidden // 32 * 8
+        return self.xq[: self.rows * rb].cpu().numpy().reshape(self.rows, rb)
+
+    def hq_host(self) -> np.ndarray:
+        rb = self.n_ff + self.n_ff // 32 * 8
+        return self.hq[: self.rows * rb].cpu().numpy().reshape(self.rows, rb)
+
+    def gu_host(self) -> np.ndarray:
+        return self.gu[: self.rows].cpu().numpy()
+
+    def dm_host(self) -> np.ndarray:
+        return self.dm[: self.rows].cpu().numpy()
+
+    def close(self):
+        self.plan.close()

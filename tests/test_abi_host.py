@@ -1,0 +1,167 @@
+"""The C ABI on the host (no GPU): exported symbols, size queries, the plan's
+host logic against the oracle's plan, and every validation error that can be
+forced before any HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import oracle
+from quantized_moe_expert_scatter_amd import _lib
+from quantized_moe_expert_scatter_amd import workloads as wl
+from tests.test_oracle_swiglu_plan import check_plan_invariants
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_prefill.h")
+FAKE_BASE = 1 << 20          # an aligned stand-in address: host-only plans never touch it
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+def test_every_declared_symbol_is_exported():
+    L = _lib.lib()
+    decl = declared_functions()
+    assert len(decl) >= 12
+    for name in decl:
+        assert hasattr(L, name), name
+    assert sorted(decl) == sorted(_lib.EXPORTS)
+
+
+def test_size_queries():
+    assert _lib.moe_q8_1_bytes(3, 64) == 3 * 80
+    assert _lib.moe_q8_1_bytes(163840, 2560) == 163840 * 3200
+    assert _lib.moe_q8_1_bytes(2, 48) == 0
+    assert _lib.moe_weight_bytes(1, 1280, 2560) == 921600
+    assert _lib.moe_weight_bytes(2, 2560, 640) == 921600
+    assert _lib.moe_weight_bytes(1, 2560, 640) == 460800
+    assert _lib.moe_weight_bytes(1, 64, 96) == 0
+    assert _lib.moe_weight_bytes(3, 64, 64) == 0
+    assert _lib.moe_plan_device_bytes(64, 2, 8, 64) > 0
+    assert _lib.moe_plan_device_bytes(64, 2, 8, 65) == 0
+    assert _lib.moe_plan_device_bytes(-1, 2, 8, 64) == 0
+    for s in (0, -1, -2, -3, -4, -5, -6):
+        assert _lib.status_string(s)
+
+
+def _weights(cfg, base=FAKE_BASE, shuffle=False, down_type=None):
+    F, H, E = cfg.n_ff, cfg.hidden, cfg.n_expert
+    dt = cfg.down_type if down_type is None else down_type
+    gu_per = _lib.moe_weight_bytes(1, 2 * F, H)
+    dn_per = _lib.moe_weight_bytes(dt, H, F)
+    gu_off = np.arange(E, dtype=np.uint64) * np.uint64(gu_per)
+    dn_off = np.arange(E, dtype=np.uint64) * np.uint64(dn_per)
+    if shuffle:
+        gu_off = gu_off[::-1].copy()
+    w_gu = _lib.Weights(1, 2 * F, H, E, base, gu_per * E, gu_off)
+    cb = wl.nl4_codebook(1) if dt == 2 else None
+    w_dn = _lib.Weights(dt, H, F, E, base, dn_per * E, dn_off, cb)
+    return w_gu, w_dn
+
+
+@pytest.mark.parametrize("kind,T,E,K,C", [("uniform", 64, 8, 2, 64), ("lognormal", 700, 64, 6, 16),
+                                          ("uniform", 33, 16, 4, 1), ("lognormal", 2048, 512, 10, 64)])
+def test_host_plan_matches_oracle(kind, T, E, K, C):
+    ids = (wl.routing_uniform(T, E, K, seed=T) if kind == "uniform"
+           else wl.routing_lognormal(T, E, K, 1.0, seed=T))
+    cfg = wl.small_config("p", T, 128, 64, E, K)
+    w_gu, w_dn = _weights(cfg)
+    plan = _lib.moe_prefill_plan(ids, E, C, w_gu, w_dn, workspace=None)
+    counts, offsets, perm, chunks = plan.query()
+    ref = oracle.plan(ids, E, C)
+    assert np.array_equal(counts, ref.counts)
+    assert np.array_equal(offsets, ref.offsets)
+    assert np.array_equal(perm, ref.perm)
+    assert np.array_equal(chunks, ref.chunks)
+    check_plan_invariants(ids, E, C, counts, offsets, perm, chunks)
+    plan.close()
+
+
+def test_empty_plan():
+    cfg = wl.small_config("p", 1, 128, 64, 4, 2)
+    w_gu, w_dn = _weights(cfg)
+    plan = _lib.moe_prefill_plan(np.zeros((0, 2), np.int32), 4, 64, w_gu, w_dn)
+    counts, offsets, perm, chunks = plan.query()
+    assert counts.tolist() == [0, 0, 0, 0] and perm.size == 0 and chunks.size == 0
+
+
+def _plan_status(ids, E, C, w_gu, w_dn, ws_ptr=None, ws_bytes=0):
+    L = _lib.lib()
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    h = ctypes.c_void_p()
+    st = L.moe_prefill_plan(ids.ctypes.data, ids.shape[0], ids.shape[1], E, C,
+                            ctypes.byref(w_gu.struct), ctypes.byref(w_dn.struct),
+                            ws_ptr, ws_bytes, None, ctypes.byref(h))
+    if st == 0:
+        L.moe_plan_destroy(h.value)
+    else:
+        assert h.value is None
+    return st
+
+
+def test_validation_errors():
+    cfg = wl.small_config("v", 8, 128, 64, 4, 2)
+    ids = wl.routing_uniform(8, 4, 2, seed=1)
+    good = _weights(cfg)
+    assert _plan_status(ids, 4, 64, *good) == 0
+    # routing
+    assert _plan_status(np.array([[0, 4]]), 4, 64, *good) == -1
+    assert _plan_status(np.array([[0, -1]]), 4, 64, *good) == -1
+    assert _plan_status(ids, 4, 0, *good) == -1
+    assert _plan_status(ids, 4, 65, *good) == -1
+    # weights
+    w_gu, w_dn = _weights(cfg)
+    w_gu.struct.base = FAKE_BASE + 8
+    assert _plan_status(ids, 4, 64, w_gu, w_dn) == -2
+    w_gu, w_dn = _weights(cfg)
+    w_gu.offsets[1] += 8
+    assert _plan_status(ids, 4, 64, w_gu, w_dn) == -2
+    w_gu, w_dn = _weights(cfg)
+    w_gu.struct.base_bytes -= 16
+    assert _plan_status(ids, 4, 64, w_gu, w_dn) == -4
+    w_gu, w_dn = _weights(cfg)
+    w_gu.struct.type = 3
+    assert _plan_status(ids, 4, 64, w_gu, w_dn) == -3
+    w_gu, w_dn = _weights(cfg)
+    w_gu.struct.type = 2                       # NL4 gate/up is not supported
+    assert _plan_status(ids, 4, 64, w_gu, w_dn) == -3
+    w_gu, w_dn = _weights(cfg)
+    w_gu.struct.cols = 96                      # not a multiple of 64 for Q2_0
+    w_dn.struct.rows = 96
+    assert _plan_status(ids, 4, 64, w_gu, w_dn) == -3
+    w_gu, w_dn = _weights(cfg)
+    w_dn.struct.rows = 64                      # down rows must equal hidden
+    assert _plan_status(ids, 4, 64, w_gu, w_dn) == -1
+    w_gu, w_dn = _weights(cfg, down_type=2)
+    assert _plan_status(ids, 4, 64, w_gu, w_dn) == 0
+    w_dn.struct.codebook = None
+    assert _plan_status(ids, 4, 64, w_gu, w_dn) == -1
+    w_gu, w_dn = _weights(cfg)
+    w_gu.struct.n_expert = 5
+    assert _plan_status(ids, 4, 64, w_gu, w_dn) == -1
+    w_gu, w_dn = _weights(cfg)
+    w_gu.struct.base = None
+    assert _plan_status(ids, 4, 64, w_gu, w_dn) == -1
+    # device workspace: misaligned, too small (rejected before any HIP call)
+    need = _lib.moe_plan_device_bytes(8, 2, 4, 64)
+    assert _plan_status(ids, 4, 64, *good, ws_ptr=FAKE_BASE + 4, ws_bytes=need) == -2
+    assert _plan_status(ids, 4, 64, *good, ws_ptr=FAKE_BASE, ws_bytes=need - 16) == -4
+
+
+def test_host_only_plan_refuses_kernels():
+    cfg = wl.small_config("v", 8, 128, 64, 4, 2)
+    ids = wl.routing_uniform(8, 4, 2, seed=1)
+    plan = _lib.moe_prefill_plan(ids, 4, 64, *_weights(cfg))
+    L = _lib.lib()
+    for f in (L.quantize_scatter, L.expert_gate_up, L.swiglu_q8, L.expert_down):
+        assert f(plan.handle, FAKE_BASE, FAKE_BASE, None) == -6
+    assert L.moe_debug_block_dots(plan.handle, 0, FAKE_BASE, 0, 1, FAKE_BASE, None) == -6
+    assert L.quantize_scatter(None, FAKE_BASE, FAKE_BASE, None) == -1
+    with pytest.raises(_lib.MoeError):
+        _lib.expert_gate_up(plan, None, None, stream=0)

@@ -36,12 +36,30 @@ def test_swiglu_against_fp64():
     assert np.all(np.abs(h - ref) <= tol)
 
 
+def test_swiglu_exp_is_correctly_rounded():
+    """e^-g inside silu is the binary32 value nearest to the exact
+    exponential: pinned by a 60-digit decimal exponential rounded with exact
+    rational arithmetic; the rest is one fp32 add, divide and multiply."""
+    from decimal import Context, Decimal
+    from fractions import Fraction
+    from tests.oracle_pins import round_to_f32
+    ctx = Context(prec=60)
+    rng = np.random.default_rng(5)
+    g = (rng.standard_normal(3000) * 5).astype(np.float32)
+    u = rng.standard_normal(3000).astype(np.float32)
+    for gi, ui in zip(g, u):
+        e = round_to_f32(Fraction(ctx.exp(Decimal(-float(gi)))))
+        silu = np.float32(gi) / (np.float32(1.0) + e)
+        assert oracle.swiglu(gi, ui) == np.float32(silu * ui), (gi, ui)
+
+
 def test_swiglu_special_values():
     assert oracle.swiglu(0.0, 5.0) == 0.0
     assert oracle.swiglu(3.0, 0.0) == 0.0
     assert oracle.swiglu(-200.0, 2.0) == 0.0          # exp overflows: silu -> -0
     assert oracle.swiglu(100.0, 2.0) == 200.0          # silu(g) = g once exp(-g) < ulp
-    assert oracle.swiglu(1.0, 1.0) == np.float32(1.0 / (1.0 + np.exp(-1.0)))
+    ref = 1.0 / (1.0 + np.exp(-1.0))
+    assert abs(oracle.swiglu(1.0, 1.0) - ref) <= 2 * np.spacing(np.float32(ref))
 
 
 def test_swiglu_q8_zero_and_huge_rows():
