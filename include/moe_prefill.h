@@ -34,7 +34,8 @@
  *     block b holds values 32b..32b+31 with d = max|x|/127 (fp32 divide),
  *     q = x/d rounded half away from zero and clamped to [-127, 127],
  *     s = sum of the block's q; a block with d == 0 is all zeros.
- *   Q2_0 matrix [rows x cols] (cols % 64 == 0), rows*cols/64*18 bytes:
+ *   Q2_0 matrix [rows x cols] (cols % 64 == 0), rows*cols/64*18 bytes
+ *   (scales must satisfy |2d| <= 65504, so that d*(code-2) is a binary16):
  *       codes plane: rows*cols/64 blocks of 16 bytes, row-major (row, block);
  *         value 16*j+b of a block is bits 2j..2j+1 of byte b; weight = d*(code-2)
  *       scales plane: rows*cols/64 binary16 d, same order, right after the codes.
@@ -118,7 +119,8 @@ size_t moe_plan_device_bytes(int tokens, int topk, int n_expert, int chunk_rows)
  *   ids_host   host int32 [tokens*topk], ids_host[t*topk+k] = k-th expert of
  *              token t, each in [0, n_expert).  A token may name an expert
  *              twice; that gives two rows.
- *   chunk_rows 1..64: rows per chunk (64 is the pages' choice).
+ *   chunk_rows 1..128: rows per chunk (the pages take 64-row chunks; one
+ *              workgroup processes one chunk against 256 weight rows).
  *   w_gu       gate/up weights: Q2_0, rows = 2*n_ff, cols = hidden.
  *   w_down     down weights: Q2_0 or NL4, rows = hidden, cols = n_ff.
  *   plan_dev   device workspace of moe_plan_device_bytes(...) bytes, 16-byte

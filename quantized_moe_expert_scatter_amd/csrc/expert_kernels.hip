@@ -4,104 +4,411 @@
 // experts; workgroups take row chunks of the experts from a chunk table,
 // largest expert first, each expert at its own row count; each weight block is
 // decoded once per pass; every product keeps the int8 values, the scales and
-// a per-32-value fp32 epilogue in K order, the 32-value integer sums being
-// exact.  PR #2145 (description): Q2_0 weights, int8 MMA with int32 sums,
-// and a magic constant fed to the accumulator input.
+// a per-32-value fp32 epilogue in K order, the integer sum of a 32-value
+// block being exact.  PR #2145 (description): Q2_0 weights, int32 sums exact
+// in any order, a kernel bound by its fp32 epilogue rather than its matrix
+// unit.
 //
-// gfx950 design:
-//  * A workgroup is one chunk (<= 64 expert-sorted activation rows) against a
-//    tile of 256 weight rows of that chunk's expert; its 4 wavefronts own 64
-//    weight rows each.  The chunk's q8_1 rows are staged K-step by K-step in
-//    LDS (shared by the 4 wavefronts); each wavefront streams its own weight
-//    rows straight from HBM into registers and decodes every weight block
-//    once, then reuses it against both 32-row activation tiles.
-//  * v_mfma_i32_32x32x32_i8: K = 32 is exactly one q8_1 block, so each MFMA
-//    yields the exact int32 dot of one 32-value block for a 32x32 tile.  A =
-//    activation rows, B = weight rows: a lane's 16 results share one weight
-//    row (one scale d_w) and cover 16 activation rows.
-//  * The accumulator input C is the bit pattern of 1.5 * 2^23, so
-//    D = bits(1.5 * 2^23) + dot and, read as a float, D is 1.5 * 2^23 + dot
-//    exactly.  fmaf(d_w, D, -d_w * 1.5 * 2^23) is then d_w * dot rounded once
-//    (exact for Q2_0, whose 11-bit scale times a 14-bit dot fits in 24 bits),
-//    and fmaf(d_x, that, acc) is the per-32-value epilogue step: two VALU
-//    operations per (row, output, block) and no int-to-float conversion.
+// gfx950 design (fp16 matrix cores, weights in registers, activations in LDS):
+//  * A workgroup is one chunk of up to 128 expert-sorted activation rows of
+//    one expert against 256 of that expert's weight rows (the N tile); each of
+//    its 4 wavefronts owns 64 weight rows (four 16-row tiles).
+//  * For each 64-value K stage the workgroup converts the chunk's q8_1 values
+//    to fp16 once and stages them in LDS (double buffered); each wavefront
+//    decodes its own weight blocks straight into MFMA operand registers, so
+//    every weight block is decoded exactly once and never round-trips
+//    through LDS, and every activation operand read from LDS feeds four
+//    weight tiles.
+//  * The contraction runs on v_mfma_f32_16x16x32_f16 (K = 32: one q8_1 block
+//    per MFMA, 4 result registers, so several MFMAs stay in flight).  The activation q (int8)
+//    is exact in fp16; a Q2_0 weight d*(c-2) is exact in fp16 (d is binary16,
+//    c-2 in {-2..1}).  Every partial sum of a 32-value block is an integer
+//    multiple of d's last bit below 2^24 in magnitude, so the MFMA of a block
+//    returns d*dot exactly -- the exact int32 block dot scaled by the
+//    block's weight scale.  The per-32-value epilogue
+//        acc = fmaf(dx, d * dot, acc)
+//    is then one VALU operation per (row, output, block), bit for bit the
+//    oracle's.  NL4 codebook entries are exact in fp16 too; there the MFMA
+//    returns the dot itself and the epilogue is fmaf(dx, d * dot, acc) with
+//    the product rounded once, as the oracle rounds it.
+//  * MFMA operands: A = weights (lane l: weight row l%16), B = activations
+//    (lane l: activation row l%16); value 8kg + p of a 32-value block goes
+//    to lane group kg = l/16, slot p.  A lane's 4 results share one
+//    activation row (one dx per block) and cover 4 consecutive weight rows,
+//    stored as one float4.
+//  * Raw weight and activation bytes are loaded 2-6 stages ahead of their use
+//    (deeper when the chunk has fewer rows and registers allow); every load
+//    is unconditional from a clamped, in-bounds
+//    address, so no in-flight register is copied (a copy would make the
+//    compiler wait for every outstanding load).
 //  * Work lists are grouped per XCD (workgroup id i runs on XCD i % 8): all
-//    chunks of an expert land on one XCD, so the 5 or 10 weight tiles and
-//    the chunk's activation rows are re-read from that XCD's L2.
+//    chunks of an expert land on one XCD, so its weight tiles and activation
+//    rows are re-read from that XCD's L2.
 #include "internal.h"
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 namespace moe {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
-typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
-constexpr int kKStep = 256;                 // contraction values staged per step
-constexpr int kQStride = kKStep + 16;       // LDS bytes per activation row (padded)
-constexpr float kMagicF = 12582912.0f;      // 1.5 * 2^23
+constexpr int kKS = 64;                 // contraction values per stage
+constexpr int kARow = kKS * 2 + 16;     // LDS bytes per staged activation row (padded)
+constexpr int kMaxRows = 128;           // activation rows per chunk (4 tiles of 32)
+constexpr int kWaves = 4;               // each owns 64 weight rows of the 256-row N tile
 
-// Q2_0 block -> the 16 signed int8 weights a lane feeds to the MFMA.
-// Lane group g (lanes 32g..32g+31) supplies values 16g..16g+15 of a 32-value
-// half h; those are field j = 2h + g (bits 2j..2j+1) of the block's 16 bytes.
-// v_perm_b32 maps each 2-bit code c to the byte c - 2 through the table
-// {0xFE, 0xFF, 0x00, 0x01} (given in both sources so selectors 0-3 and 4-7
-// agree).
-__device__ __forceinline__ v4i q2_0_operand(const uint4 &codes, int j) {
-    const uint32_t kTable = 0x0100FFFEu;
-    const int sh = 2 * j;
-    v4i r;
-    r.x = __builtin_amdgcn_perm(kTable, kTable, (codes.x >> sh) & 0x03030303u);
-    r.y = __builtin_amdgcn_perm(kTable, kTable, (codes.y >> sh) & 0x03030303u);
-    r.z = __builtin_amdgcn_perm(kTable, kTable, (codes.z >> sh) & 0x03030303u);
-    r.w = __builtin_amdgcn_perm(kTable, kTable, (codes.w >> sh) & 0x03030303u);
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__device__ __forceinline__ v2h as_v2h(uint32_t x) {
+    v2h r;
+    __builtin_memcpy(&r, &x, 4);
     return r;
 }
 
-// NL4 block -> 16 int8 codebook entries: lane group 0 takes the low nibbles
-// (values 0..15), group 1 the high nibbles (values 16..31).  Two byte-select
-// lookups (entries 0-7 and 8-15) are merged on bit 3 of each code.
-__device__ __forceinline__ uint32_t nl4_lookup(uint32_t c, uint32_t cb0, uint32_t cb1,
-                                               uint32_t cb2, uint32_t cb3) {
+__device__ __forceinline__ uint32_t as_u32(v2h x) {
+    uint32_t r;
+    __builtin_memcpy(&r, &x, 4);
+    return r;
+}
+
+__device__ __forceinline__ v8h pack8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    v8h r;
+    const uint32_t w[4] = {a, b, c, d};
+    __builtin_memcpy(&r, w, 16);
+    return r;
+}
+
+// 4 int8 -> 4 fp16 (two packed pairs), exact: byte b becomes the fp16
+// 1024 + (b ^ 0x80) = 1152 + q, then 1152 is subtracted.
+__device__ __forceinline__ void i8x4_to_f16(uint32_t w, uint32_t &lo, uint32_t &hi) {
+    const uint32_t u = w ^ 0x80808080u;
+    const v2h bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    lo = as_u32(as_v2h(perm(0x64646464u, u, 0x05010400u)) + bias);
+    hi = as_u32(as_v2h(perm(0x64646464u, u, 0x07030602u)) + bias);
+}
+
+// Q2_0: four 2-bit codes, one per byte of c (values 0..3) -> four fp16
+// weights d*(c-2).  The table holds the four fp16 values {-2d, -d, 0, d}:
+// low bytes in tlo, high bytes in thi, so code c selects byte c and c+4.
+__device__ __forceinline__ void q2_to_f16(uint32_t c, uint32_t thi, uint32_t tlo, uint32_t &h01,
+                                          uint32_t &h23) {
+    const uint32_t c4 = c | 0x04040404u;
+    h01 = perm(thi, tlo, perm(c4, c, 0x05010400u));
+    h23 = perm(thi, tlo, perm(c4, c, 0x07030602u));
+}
+
+// NL4: four 4-bit codes (low nibbles of the bytes of c) -> four int8
+// codebook entries: two byte-select lookups (entries 0-7 and 8-15) merged
+// on bit 3 of each code (selector 0x0C yields 0x00, 0x0D yields 0xFF).
+__device__ __forceinline__ uint32_t nl4_lookup(uint32_t c, const uint32_t (&cb)[4]) {
     const uint32_t lo3 = c & 0x07070707u;
-    const uint32_t lo = __builtin_amdgcn_perm(cb1, cb0, lo3);   // entries 0..7
-    const uint32_t hi = __builtin_amdgcn_perm(cb3, cb2, lo3);   // entries 8..15
-    // selector 0x0C yields 0x00 and 0x0D yields 0xFF
-    const uint32_t msel = ((c >> 3) & 0x01010101u) | 0x0C0C0C0Cu;
-    const uint32_t mask = __builtin_amdgcn_perm(0u, 0u, msel);
+    const uint32_t lo = perm(cb[1], cb[0], lo3);
+    const uint32_t hi = perm(cb[3], cb[2], lo3);
+    const uint32_t mask = perm(0u, 0u, ((c >> 3) & 0x01010101u) | 0x0C0C0C0Cu);
     return (hi & mask) | (lo & ~mask);
 }
 
-__device__ __forceinline__ v4i nl4_operand(const uint4 &codes, int g, const uint32_t (&cb)[4]) {
-    const int sh = 4 * g;
-    v4i r;
-    r.x = nl4_lookup((codes.x >> sh) & 0x0F0F0F0Fu, cb[0], cb[1], cb[2], cb[3]);
-    r.y = nl4_lookup((codes.y >> sh) & 0x0F0F0F0Fu, cb[0], cb[1], cb[2], cb[3]);
-    r.z = nl4_lookup((codes.z >> sh) & 0x0F0F0F0Fu, cb[0], cb[1], cb[2], cb[3]);
-    r.w = nl4_lookup((codes.w >> sh) & 0x0F0F0F0Fu, cb[0], cb[1], cb[2], cb[3]);
-    return r;
-}
-
-__device__ __forceinline__ float half_bits_to_float(uint16_t h) {
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+    const uint16_t b = uint16_t(h);
     _Float16 v;
-    __builtin_memcpy(&v, &h, 2);
+    __builtin_memcpy(&v, &b, 2);
     return static_cast<float>(v);
 }
 
-// Output row of MFMA result register v for lane group g (32x32 layout).
-__device__ __forceinline__ int tile_row(int v, int g) { return (v & 3) + 8 * (v >> 2) + 4 * g; }
+// Raw weight bytes of one lane for one stage and one 16-row weight tile: the
+// 8 code bytes its lane group reads (Q2_0: bytes 8(kg&1)..+7 of the block,
+// which hold the fields of both halves; NL4: the same 8 bytes of each of the
+// two blocks) and the scale(s).
+struct WRaw {
+    uint2 c0, c1;
+    uint32_t s;
+};
+
+// Raw bytes of one staged activation block: 32 q bytes and the scale.
+struct ARaw {
+    uint4 q0, q1;
+    float d;
+};
+
+template <int WTYPE>
+__device__ __forceinline__ WRaw load_weights(const uint8_t *codes, const uint16_t *scales, int n,
+                                             int nbw, int k0, int kg) {
+    WRaw w;
+    const int off = 8 * (kg & 1);
+    if constexpr (WTYPE == 1) {
+        const size_t blk = size_t(n) * nbw + (k0 >> 6);
+        w.c0 = *reinterpret_cast<const uint2 *>(codes + blk * 16 + off);
+        w.c1 = w.c0;
+        w.s = scales[blk];
+    } else {
+        // the second block of a half-filled last stage is clamped to the first
+        const size_t blk = size_t(n) * nbw + (k0 >> 5);
+        const size_t blk1 = (k0 >> 5) + 1 < nbw ? blk + 1 : blk;
+        w.c0 = *reinterpret_cast<const uint2 *>(codes + blk * 16 + off);
+        w.c1 = *reinterpret_cast<const uint2 *>(codes + blk1 * 16 + off);
+        w.s = uint32_t(scales[blk]) | (uint32_t(scales[blk1]) << 16);
+    }
+    return w;
+}
+
+// The 8 fp16 weights lane group kg feeds to the MFMA for 32-value block h of
+// the stage: values 8kg..8kg+7 of the block.  Q2_0 half h: value 32h+8kg+p
+// is field 2h + kg/2 of byte 8(kg&1) + p.  NL4 block h: value 8kg+p is the
+// low (kg < 2) or high nibble of byte 8(kg&1) + p.
+template <int WTYPE>
+__device__ __forceinline__ v8h decode_ops(const WRaw &w, int h, int kg, uint32_t thi, uint32_t tlo,
+                                          const uint32_t (&cb)[4]) {
+    uint32_t r[4];
+    if constexpr (WTYPE == 1) {
+        const int sh = 2 * (2 * h + (kg >> 1));
+        q2_to_f16((w.c0.x >> sh) & 0x03030303u, thi, tlo, r[0], r[1]);
+        q2_to_f16((w.c0.y >> sh) & 0x03030303u, thi, tlo, r[2], r[3]);
+    } else {
+        const uint2 c = h == 0 ? w.c0 : w.c1;
+        const int sh = 4 * (kg >> 1);
+        i8x4_to_f16(nl4_lookup((c.x >> sh) & 0x0F0F0F0Fu, cb), r[0], r[1]);
+        i8x4_to_f16(nl4_lookup((c.y >> sh) & 0x0F0F0F0Fu, cb), r[2], r[3]);
+    }
+    return pack8(r[0], r[1], r[2], r[3]);
+}
+
+// The fp16 table {-2d, -d, 0, d} of a Q2_0 block scale, split into low and
+// high bytes (code c selects byte c of tlo and byte c of thi).
+__device__ __forceinline__ void q2_table(uint32_t hb, uint32_t &thi, uint32_t &tlo) {
+    _Float16 d;
+    const uint16_t hb16 = uint16_t(hb);
+    __builtin_memcpy(&d, &hb16, 2);
+    const _Float16 d2 = d * (_Float16)2.0f;   // exact unless it overflows binary16
+    uint16_t b2;
+    __builtin_memcpy(&b2, &d2, 2);
+    const uint32_t m2 = b2 ^ 0x8000u, m1 = hb ^ 0x8000u, p1 = hb;
+    tlo = (m2 & 0xFFu) | ((m1 & 0xFFu) << 8) | ((p1 & 0xFFu) << 24);
+    thi = (m2 >> 8) | ((m1 >> 8) << 8) | ((p1 >> 8) << 24);
+}
+
+__device__ __forceinline__ ARaw load_acts(const uint8_t *row, int cols, int kb) {
+    ARaw a;
+    a.q0 = *reinterpret_cast<const uint4 *>(row + 32 * kb);
+    a.q1 = *reinterpret_cast<const uint4 *>(row + 32 * kb + 16);
+    a.d = reinterpret_cast<const float *>(row + cols)[kb];
+    return a;
+}
+
+// Convert one staged activation block to fp16 and store it in LDS.
+__device__ __forceinline__ void stage_acts(const ARaw &a, uint8_t *dst, float *dx) {
+    const uint32_t q[8] = {a.q0.x, a.q0.y, a.q0.z, a.q0.w, a.q1.x, a.q1.y, a.q1.z, a.q1.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint4 o;
+        i8x4_to_f16(q[2 * i], o.x, o.y);
+        i8x4_to_f16(q[2 * i + 1], o.z, o.w);
+        *reinterpret_cast<uint4 *>(dst + 16 * i) = o;
+    }
+    *dx = a.d;
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+struct Lds {
+    uint8_t act[2][kMaxRows * kARow];   // staged fp16 activations, double buffered
+    float dx[2][2][kMaxRows];           // their block scales
+    float dw[kWaves][2][4][16];         // NL4: block scales of each wave's weight rows
+};
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// The whole K loop of one work item.  Each wave owns 64 weight rows (four
+// 16-row tiles) and runs them against NA 16-row activation tiles (the chunk's
+// rows rounded up; rows past the chunk are never stored).
+template <int WTYPE, bool DOTS, int NA>
+__device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int expert, int row0,
+                                         int nrows, int n0) {
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int kg = lane >> 4;                    // k group of the MFMA operands
+    const int col = lane & 15;
+    const int cols = a.cols;
+    const int nb32 = cols >> 5;
+    const size_t arb = size_t(cols) + size_t(nb32) * 8;
+    constexpr int WB = WTYPE == 1 ? 64 : 32;
+    const int nbw = cols / WB;
+    const int n_stages = (cols + kKS - 1) / kKS;
+    const int last_k = (n_stages - 1) * kKS;
+
+    // weights: this lane's row in each of the wave's four tiles (clamped for loads)
+    const uint8_t *wexp = a.w_base + a.w_off[expert];
+    const uint16_t *wscales = reinterpret_cast<const uint16_t *>(wexp + size_t(a.out_rows) * nbw * 16);
+    const int nw = n0 + 64 * wave;
+    const bool wave_on = nw < a.out_rows;
+    int wr[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) wr[t] = min(nw + 16 * t + col, a.out_rows - 1);
+    uint32_t cb[4] = {0u, 0u, 0u, 0u};
+    if constexpr (WTYPE == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            cb[i] = uint32_t(uint8_t(a.codebook[4 * i])) | (uint32_t(uint8_t(a.codebook[4 * i + 1])) << 8) |
+                    (uint32_t(uint8_t(a.codebook[4 * i + 2])) << 16) |
+                    (uint32_t(uint8_t(a.codebook[4 * i + 3])) << 24);
+    }
+    auto wload = [&](int stage, int t) {
+        return load_weights<WTYPE>(wexp, wscales, wr[t], nbw, min(stage * kKS, last_k), kg);
+    };
+
+    // activations: thread tid stages row tid/2 (clamped), block tid&1 of a stage
+    const int srow = tid >> 1;
+    const int sblk = tid & 1;
+    const uint8_t *sact = a.act + size_t(row0 + min(srow, nrows - 1)) * arb;
+    auto aload = [&](int stage) {
+        const int kb = min(stage * kKS, last_k) / 32 + sblk;
+        return load_acts(sact, cols, min(kb, nb32 - 1));
+    };
+
+    v4f acc[4][NA];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < NA; ++r) acc[t][r] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // U register slots; the stage loop is unrolled by U so every slot is a
+    // fixed register set.  The weights of stage x sit in wslot[x % U] and are
+    // loaded U stages before use; the activations of stage x sit in
+    // aslot[x % U], loaded U-1 stages before they are staged into LDS.  Each
+    // stage issues its activation load before its weight load (vmcnt retires
+    // loads in order).  Fewer activation tiles leave registers for a deeper
+    // prefetch.
+    constexpr int U = NA >= 8 ? 2 : (NA >= 4 ? 3 : (NA >= 2 ? 4 : 6));
+    WRaw wslot[U][4];
+    ARaw aslot[U];
+#pragma unroll
+    for (int x = 0; x < U; ++x) {
+        aslot[x] = aload(x);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) wslot[x][t] = wload(x, t);
+    }
+    stage_acts(aslot[0], &L.act[0][srow * kARow + 64 * sblk], &L.dx[0][sblk][srow]);
+    __syncthreads();
+
+    auto stage = [&](auto J, int s) {
+        constexpr int j = decltype(J)::value;           // s % U
+        constexpr int jn = (j + 1) % U;
+        const int par = s & 1;
+        const int k0 = s * kKS;
+        const int nv = min(kKS, cols - k0);
+        const int nblk = WTYPE == 1 ? 2 : (nv >> 5);
+
+        if (wave_on) {
+            uint32_t thi[4] = {0u, 0u, 0u, 0u}, tlo[4] = {0u, 0u, 0u, 0u};
+            if constexpr (WTYPE == 1) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) q2_table(DOTS ? 0x3C00u : (wslot[j][t].s & 0xFFFFu), thi[t], tlo[t]);
+            } else {
+                // publish this lane's row scales for the epilogue
+                if (kg == 0) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        L.dw[wave][0][t][col] = half_bits_to_float(wslot[j][t].s & 0xFFFFu);
+                        L.dw[wave][1][t][col] = half_bits_to_float(wslot[j][t].s >> 16);
+                    }
+                }
+                __builtin_amdgcn_wave_barrier();
+            }
+            const uint8_t *abuf = L.act[par];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if (h < nblk) {
+                    v8h wop[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) wop[t] = decode_ops<WTYPE>(wslot[j][t], h, kg, thi[t], tlo[t], cb);
+                    v4f dwv[4];
+                    if constexpr (WTYPE == 2) {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            dwv[t] = *reinterpret_cast<const v4f *>(&L.dw[wave][h][t][4 * kg]);
+                    }
+#pragma unroll
+                    for (int r = 0; r < NA; ++r) {
+                        const uint8_t *src = abuf + (r * 16 + col) * kARow + (32 * h + 8 * kg) * 2;
+                        const v8h bop = *reinterpret_cast<const v8h *>(src);
+                        const float dx = L.dx[par][h][r * 16 + col];
+                        v4f d[4];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            d[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop[t], bop, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                        if constexpr (DOTS) {
+                            const int arow = r * 16 + col;
+                            const int rr = row0 + arow - a.dots_row_begin;
+                            if (arow < nrows && rr >= 0 && rr < a.dots_n_rows) {
+#pragma unroll
+                                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                                    for (int v = 0; v < 4; ++v)
+                                        a.dots[(size_t(rr) * a.out_rows + nw + 16 * t + 4 * kg + v) * nb32 + (k0 >> 5) + h] =
+                                            int(d[t][v]);
+                            }
+                        } else if constexpr (WTYPE == 1) {
+#pragma unroll
+                            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                                for (int v = 0; v < 4; ++v) acc[t][r][v] = __builtin_fmaf(dx, d[t][v], acc[t][r][v]);
+                        } else {
+#pragma unroll
+                            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                                for (int v = 0; v < 4; ++v)
+                                    acc[t][r][v] = __builtin_fmaf(dx, dwv[t][v] * d[t][v], acc[t][r][v]);
+                        }
+                    }
+                }
+            }
+        }
+
+        if (s + 1 < n_stages)
+            stage_acts(aslot[jn], &L.act[par ^ 1][srow * kARow + 64 * sblk], &L.dx[par ^ 1][sblk][srow]);
+        aslot[j] = aload(s + U);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) wslot[j][t] = wload(s + U, t);
+        __syncthreads();
+    };
+
+    for (int s0 = 0; s0 < n_stages; s0 += U)
+        static_for<0, U>([&](auto J) {
+            const int s = s0 + decltype(J)::value;
+            if (s < n_stages) stage(J, s);
+        });
+
+    if constexpr (!DOTS) {
+        if (!wave_on) return;
+#pragma unroll
+        for (int r = 0; r < NA; ++r) {
+            const int arow = r * 16 + col;
+            if (arow >= nrows) continue;
+            const int rr = row0 + arow;
+            const size_t orow = a.perm ? size_t(a.perm[rr]) : size_t(rr);
+            float *dst = a.out + orow * a.out_rows + nw + 4 * kg;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) *reinterpret_cast<v4f *>(dst + 16 * t) = acc[t][r];
+        }
+    }
+}
 
 template <int WTYPE, bool DOTS>
 __global__ __launch_bounds__(256, 2) void expert_product_kernel(ProductArgs a) {
-    constexpr int WB = WTYPE == 1 ? 64 : 32;       // values per weight block
-    constexpr int HALVES = WB / 32;                // q8_1 blocks per weight block
-    constexpr int MAXWB = kKStep / WB;             // weight blocks per K-step
+    __shared__ __attribute__((aligned(16))) Lds L;
 
-    __shared__ __attribute__((aligned(16))) uint8_t q_lds[64 * kQStride];
-    __shared__ __attribute__((aligned(16))) float dx_lds[(kKStep / 32) * 64];
-
-    // ---- work item: (chunk, weight tile) from this XCD's list
+    // work item: (chunk, weight tile) from this XCD's list
     const int bid = blockIdx.x;
     const int xcd = bid % kXcds;
     const int j = bid / kXcds;
@@ -112,170 +419,22 @@ __global__ __launch_bounds__(256, 2) void expert_product_kernel(ProductArgs a) {
     const int expert = a.chunks[4 * c + 0];
     const int row0 = a.chunks[4 * c + 1];
     const int nrows = a.chunks[4 * c + 2];
+    const int n0 = tile * kTileRows;
 
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
-    const int g = lane >> 5;
-    const int col = lane & 31;
-    const int n_wave = tile * kTileRows + wave * 64;     // first weight row of this wave
-    const bool wave_on = n_wave < a.out_rows;
-
-    const int cols = a.cols;
-    const int nb32 = cols >> 5;
-    const size_t arb = size_t(cols) + size_t(nb32) * 8;  // q8_1 row bytes
-    const int nbw = cols / WB;                            // weight blocks per row
-    const uint8_t *wexp = a.w_base + a.w_off[expert];
-    const uint8_t *wcodes = wexp;
-    const uint16_t *wscales = reinterpret_cast<const uint16_t *>(wexp + size_t(a.out_rows) * nbw * 16);
-
-    uint32_t cb[4] = {0u, 0u, 0u, 0u};
-    if constexpr (WTYPE == 2) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            cb[i] = uint32_t(uint8_t(a.codebook[4 * i])) | (uint32_t(uint8_t(a.codebook[4 * i + 1])) << 8) |
-                    (uint32_t(uint8_t(a.codebook[4 * i + 2])) << 16) |
-                    (uint32_t(uint8_t(a.codebook[4 * i + 3])) << 24);
-    }
-
-    v16i magic;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) magic[v] = int(kMagicBits);
-
-    v16f acc[2][2];
-#pragma unroll
-    for (int at = 0; at < 2; ++at)
-#pragma unroll
-        for (int bt = 0; bt < 2; ++bt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[at][bt][v] = 0.0f;
-
-    for (int k0 = 0; k0 < cols; k0 += kKStep) {
-        const int ks = min(kKStep, cols - k0);
-        const int nbk = ks >> 5;  // q8_1 blocks in this step
-
-        __syncthreads();
-        // ---- stage the chunk's activation q bytes and scales for this step
-        {
-            const int r = tid >> 2;
-            const int seg = (tid & 3) * 64;
-            const uint8_t *src = a.act + size_t(row0 + r) * arb + k0 + seg;
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int off = seg + 16 * p;
-                if (off < ks) {
-                    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-                    if (r < nrows) v = *reinterpret_cast<const uint4 *>(src + 16 * p);
-                    *reinterpret_cast<uint4 *>(q_lds + r * kQStride + off) = v;
-                }
-            }
-            const int rr = tid & 63;
-            for (int kb = tid >> 6; kb < nbk; kb += 4) {
-                float d = 0.0f;
-                if (rr < nrows)
-                    d = reinterpret_cast<const float *>(a.act + size_t(row0 + rr) * arb + cols)[(k0 >> 5) + kb];
-                dx_lds[kb * 64 + rr] = d;
-            }
-        }
-        __syncthreads();
-        if (!wave_on) continue;
-
-        // ---- this wave's weight blocks for the step (two 32-row B tiles)
-        const int nwb = ks / WB;
-        uint4 codes[2][MAXWB];
-        float dwf[2][MAXWB];
-#pragma unroll
-        for (int bt = 0; bt < 2; ++bt) {
-            const int n = n_wave + bt * 32 + col;
-            const size_t blk0 = size_t(n) * nbw + (k0 / WB);
-#pragma unroll
-            for (int wb = 0; wb < MAXWB; ++wb) {
-                if (wb < nwb) {
-                    codes[bt][wb] = *reinterpret_cast<const uint4 *>(wcodes + (blk0 + wb) * 16);
-                    dwf[bt][wb] = half_bits_to_float(wscales[blk0 + wb]);
-                } else {
-                    codes[bt][wb] = make_uint4(0u, 0u, 0u, 0u);
-                    dwf[bt][wb] = 0.0f;
-                }
-            }
-        }
-
-#pragma unroll
-        for (int wb = 0; wb < MAXWB; ++wb) {
-            if (wb >= nwb) break;
-#pragma unroll
-            for (int h = 0; h < HALVES; ++h) {
-                const int kb = wb * HALVES + h;   // q8_1 block within the step
-                v4i bop[2];
-#pragma unroll
-                for (int bt = 0; bt < 2; ++bt) {
-                    if constexpr (WTYPE == 1)
-                        bop[bt] = q2_0_operand(codes[bt][wb], 2 * h + g);
-                    else
-                        bop[bt] = nl4_operand(codes[bt][wb], g, cb);
-                }
-#pragma unroll
-                for (int at = 0; at < 2; ++at) {
-                    const v4i aop = *reinterpret_cast<const v4i *>(
-                        q_lds + (at * 32 + col) * kQStride + kb * 32 + 16 * g);
-                    float dxv[16];
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const float4 d4 = *reinterpret_cast<const float4 *>(
-                            dx_lds + kb * 64 + at * 32 + 8 * m + 4 * g);
-                        dxv[4 * m + 0] = d4.x;
-                        dxv[4 * m + 1] = d4.y;
-                        dxv[4 * m + 2] = d4.z;
-                        dxv[4 * m + 3] = d4.w;
-                    }
-#pragma unroll
-                    for (int bt = 0; bt < 2; ++bt) {
-                        const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, bop[bt], magic, 0, 0, 0);
-                        if constexpr (DOTS) {
-                            const int n = n_wave + bt * 32 + col;
-#pragma unroll
-                            for (int v = 0; v < 16; ++v) {
-                                const int rl = at * 32 + tile_row(v, g);
-                                const int r = row0 + rl - a.dots_row_begin;
-                                if (rl < nrows && r >= 0 && r < a.dots_n_rows)
-                                    a.dots[(size_t(r) * a.out_rows + n) * nb32 + (k0 >> 5) + kb] =
-                                        D[v] - int(kMagicBits);
-                            }
-                        } else {
-                            const float dw = dwf[bt][wb];
-                            const float ndwm = -dw * kMagicF;
-#pragma unroll
-                            for (int v = 0; v < 16; ++v) {
-                                const float p = __builtin_fmaf(dw, __int_as_float(D[v]), ndwm);
-                                acc[at][bt][v] = __builtin_fmaf(dxv[v], p, acc[at][bt][v]);
-                            }
-                        }
-                    }
-                }
-            }
-        }
-    }
-
-    if constexpr (!DOTS) {
-        if (!wave_on) return;
-#pragma unroll
-        for (int at = 0; at < 2; ++at)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int rl = at * 32 + tile_row(v, g);
-                if (rl >= nrows) continue;
-                const int r = row0 + rl;
-                const size_t orow = a.perm ? size_t(a.perm[r]) : size_t(r);
-                float *dst = a.out + orow * a.out_rows + n_wave + col;
-#pragma unroll
-                for (int bt = 0; bt < 2; ++bt) dst[bt * 32] = acc[at][bt][v];
-            }
-    }
+    const int na = (nrows + 15) >> 4;          // 16-row activation tiles: 1..8
+    if (na <= 1)
+        run_item<WTYPE, DOTS, 1>(a, L, expert, row0, nrows, n0);
+    else if (na <= 2)
+        run_item<WTYPE, DOTS, 2>(a, L, expert, row0, nrows, n0);
+    else if (na <= 4)
+        run_item<WTYPE, DOTS, 4>(a, L, expert, row0, nrows, n0);
+    else
+        run_item<WTYPE, DOTS, 8>(a, L, expert, row0, nrows, n0);
 }
 
 hipError_t launch_expert_product(const ProductArgs &a, hipStream_t stream) {
     if (a.max_items <= 0) return hipSuccess;
-    const dim3 grid(kXcds * a.max_items), block(256);
+    const dim3 grid(kXcds * a.max_items), block(64 * kWaves);
     if (a.wtype == 1) {
         if (a.dots)
             hipLaunchKernelGGL((expert_product_kernel<1, true>), grid, block, 0, stream, a);

@@ -10,7 +10,7 @@
 namespace moe {
 
 constexpr int kXcds = 8;           // MI355X: 8 accelerator dies, each with its own L2
-constexpr int kMaxChunkRows = 64;  // rows of one chunk = two 32-row MFMA tiles
+constexpr int kMaxChunkRows = 128;  // rows of one chunk = four 32-row MFMA tiles
 constexpr int kTileRows = 256;     // weight rows (outputs) per workgroup: 4 waves x 64
 constexpr uint32_t kMagicBits = 0x4B400000u;  // 1.5 * 2^23 as binary32
 

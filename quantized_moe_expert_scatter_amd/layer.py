@@ -25,7 +25,7 @@ class DeviceLayer:
     """
 
     def __init__(self, x: np.ndarray, ids: np.ndarray, w_gu: ExpertWeights, w_down: ExpertWeights,
-                 chunk_rows: int = 64, device="cuda", stream=None):
+                 chunk_rows: int = 128, device="cuda", stream=None):
         import torch
         self.device = torch.device(device)
         self.tokens, self.hidden = x.shape

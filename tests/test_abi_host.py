@@ -44,7 +44,8 @@ def test_size_queries():
     assert _lib.moe_weight_bytes(1, 64, 96) == 0
     assert _lib.moe_weight_bytes(3, 64, 64) == 0
     assert _lib.moe_plan_device_bytes(64, 2, 8, 64) > 0
-    assert _lib.moe_plan_device_bytes(64, 2, 8, 65) == 0
+    assert _lib.moe_plan_device_bytes(64, 2, 8, 128) > 0
+    assert _lib.moe_plan_device_bytes(64, 2, 8, 129) == 0
     assert _lib.moe_plan_device_bytes(-1, 2, 8, 64) == 0
     for s in (0, -1, -2, -3, -4, -5, -6):
         assert _lib.status_string(s)
@@ -114,7 +115,8 @@ def test_validation_errors():
     assert _plan_status(np.array([[0, 4]]), 4, 64, *good) == -1
     assert _plan_status(np.array([[0, -1]]), 4, 64, *good) == -1
     assert _plan_status(ids, 4, 0, *good) == -1
-    assert _plan_status(ids, 4, 65, *good) == -1
+    assert _plan_status(ids, 4, 129, *good) == -1
+    assert _plan_status(ids, 4, 128, *good) == 0
     # weights
     w_gu, w_dn = _weights(cfg)
     w_gu.struct.base = FAKE_BASE + 8

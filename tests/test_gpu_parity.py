@@ -124,7 +124,7 @@ def test_swiglu_q8_and_down_alone_on_oracle_inputs(name):
     D.close()
 
 
-@pytest.mark.parametrize("chunk_rows", [1, 16, 37, 64])
+@pytest.mark.parametrize("chunk_rows", [1, 16, 37, 64, 100, 128])
 def test_schedule_invariance(chunk_rows):
     """Outputs do not depend on the chunk size, the chunk order or where the
     experts lie in memory."""
