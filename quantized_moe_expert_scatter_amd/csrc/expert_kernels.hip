@@ -12,35 +12,42 @@
 // gfx950 design (fp16 matrix cores, weights in registers, activations in LDS):
 //  * A workgroup is one chunk of up to 128 expert-sorted activation rows of
 //    one expert against 256 of that expert's weight rows (the N tile); each of
-//    its 4 wavefronts owns 64 weight rows (four 16-row tiles).
+//    its 4 wavefronts owns 64 weight rows (two 32-row tiles).
 //  * For each 64-value K stage the workgroup converts the chunk's q8_1 values
 //    to fp16 once and stages them in LDS (double buffered); each wavefront
 //    decodes its own weight blocks straight into MFMA operand registers, so
 //    every weight block is decoded exactly once and never round-trips
-//    through LDS, and every activation operand read from LDS feeds four
-//    weight tiles.
-//  * The contraction runs on v_mfma_f32_16x16x32_f16 (K = 32: one q8_1 block
-//    per MFMA, 4 result registers, so several MFMAs stay in flight).  The activation q (int8)
-//    is exact in fp16; a Q2_0 weight d*(c-2) is exact in fp16 (d is binary16,
-//    c-2 in {-2..1}).  Every partial sum of a 32-value block is an integer
-//    multiple of d's last bit below 2^24 in magnitude, so the MFMA of a block
-//    returns d*dot exactly -- the exact int32 block dot scaled by the
-//    block's weight scale.  The per-32-value epilogue
+//    through LDS, and every activation operand read from LDS feeds both of
+//    the wave's weight tiles.
+//  * The contraction runs on v_mfma_f32_32x32x16_f16: a 32-value block is two
+//    MFMAs (the second accumulating onto the first), 16 results per lane.
+//    The activation q (int8) is exact in fp16; a Q2_0 weight d*(c-2) is exact
+//    in fp16 (d is binary16, c-2 in {-2..1}).  Every partial sum of a
+//    32-value block is an integer multiple of d's last bit below 2^24 in
+//    magnitude, so the pair returns d*dot exactly -- the exact int32 block
+//    dot scaled by the block's weight scale -- whatever order the matrix unit
+//    adds in.  The per-32-value epilogue
 //        acc = fmaf(dx, d * dot, acc)
 //    is then one VALU operation per (row, output, block), bit for bit the
 //    oracle's.  NL4 codebook entries are exact in fp16 too; there the MFMA
 //    returns the dot itself and the epilogue is fmaf(dx, d * dot, acc) with
 //    the product rounded once, as the oracle rounds it.
-//  * MFMA operands: A = weights (lane l: weight row l%16), B = activations
-//    (lane l: activation row l%16); value 8kg + p of a 32-value block goes
-//    to lane group kg = l/16, slot p.  A lane's 4 results share one
-//    activation row (one dx per block) and cover 4 consecutive weight rows,
-//    stored as one float4.
+//    (On gfx950 an MFMA holds the vector ALU for a large part of its run, so
+//    the 32x32 shape, with four times the results per instruction of the
+//    16x16 one, leaves more ALU time to the epilogue.)
+//  * MFMA operands: A = weights (lane l: weight row l%32), B = activations
+//    (lane l: activation row l%32); lane half kq = l/32 holds values
+//    16g + 8kq + p (p < 8) of a 32-value block in the MFMA of half g.  Any
+//    assignment that A and B share gives the same exact sum; this one reads
+//    Q2_0 field 2h+g of bytes 8kq..8kq+7 and NL4 nibble g of the same bytes,
+//    and 16 contiguous activation bytes.  A lane's 16 results share one
+//    activation row (one dx per block) and cover weight rows
+//    8q + 4kq + i (q, i < 4), stored as four float4.
 //  * Raw weight and activation bytes are loaded 2-6 stages ahead of their use
 //    (deeper when the chunk has fewer rows and registers allow); every load
-//    is unconditional from a clamped, in-bounds
-//    address, so no in-flight register is copied (a copy would make the
-//    compiler wait for every outstanding load).
+//    is unconditional from a clamped, in-bounds address, so no in-flight
+//    register is copied (a copy would make the compiler wait for every
+//    outstanding load).
 //  * Work lists are grouped per XCD (workgroup id i runs on XCD i % 8): all
 //    chunks of an expert land on one XCD, so its weight tiles and activation
 //    rows are re-read from that XCD's L2.
@@ -54,6 +61,8 @@ namespace moe {
 
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kKS = 64;                 // contraction values per stage
 constexpr int kARow = kKS * 2 + 16;     // LDS bytes per staged activation row (padded)
@@ -120,10 +129,10 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
     return static_cast<float>(v);
 }
 
-// Raw weight bytes of one lane for one stage and one 16-row weight tile: the
-// 8 code bytes its lane group reads (Q2_0: bytes 8(kg&1)..+7 of the block,
-// which hold the fields of both halves; NL4: the same 8 bytes of each of the
-// two blocks) and the scale(s).
+// Raw weight bytes of one lane for one stage and one 32-row weight tile:
+// bytes 8kq..8kq+7 of the stage's block (Q2_0: one 64-value block, all four
+// fields; NL4: the same bytes of each of the two 32-value blocks) and the
+// scale(s) of the lane's weight row.
 struct WRaw {
     uint2 c0, c1;
     uint32_t s;
@@ -135,42 +144,41 @@ struct ARaw {
     float d;
 };
 
+// codes/scales: the expert's planes advanced to the stage (wave-uniform);
+// coff/soff: the lane's byte offset of its code bytes and element offset of
+// its scale within them (32-bit, so the loads take a scalar base).
 template <int WTYPE>
-__device__ __forceinline__ WRaw load_weights(const uint8_t *codes, const uint16_t *scales, int n,
-                                             int nbw, int k0, int kg) {
+__device__ __forceinline__ WRaw load_weights(const uint8_t *codes, const uint16_t *scales, uint32_t coff,
+                                             uint32_t soff, bool second) {
     WRaw w;
-    const int off = 8 * (kg & 1);
     if constexpr (WTYPE == 1) {
-        const size_t blk = size_t(n) * nbw + (k0 >> 6);
-        w.c0 = *reinterpret_cast<const uint2 *>(codes + blk * 16 + off);
+        w.c0 = *reinterpret_cast<const uint2 *>(codes + coff);
         w.c1 = w.c0;
-        w.s = scales[blk];
+        w.s = scales[soff];
     } else {
         // the second block of a half-filled last stage is clamped to the first
-        const size_t blk = size_t(n) * nbw + (k0 >> 5);
-        const size_t blk1 = (k0 >> 5) + 1 < nbw ? blk + 1 : blk;
-        w.c0 = *reinterpret_cast<const uint2 *>(codes + blk * 16 + off);
-        w.c1 = *reinterpret_cast<const uint2 *>(codes + blk1 * 16 + off);
-        w.s = uint32_t(scales[blk]) | (uint32_t(scales[blk1]) << 16);
+        const uint32_t o1 = second ? 16u : 0u;
+        w.c0 = *reinterpret_cast<const uint2 *>(codes + coff);
+        w.c1 = *reinterpret_cast<const uint2 *>(codes + coff + o1);
+        w.s = uint32_t(scales[soff]) | (uint32_t(scales[soff + (o1 >> 4)]) << 16);
     }
     return w;
 }
 
-// The 8 fp16 weights lane group kg feeds to the MFMA for 32-value block h of
-// the stage: values 8kg..8kg+7 of the block.  Q2_0 half h: value 32h+8kg+p
-// is field 2h + kg/2 of byte 8(kg&1) + p.  NL4 block h: value 8kg+p is the
-// low (kg < 2) or high nibble of byte 8(kg&1) + p.
-template <int WTYPE>
-__device__ __forceinline__ v8h decode_ops(const WRaw &w, int h, int kg, uint32_t thi, uint32_t tlo,
-                                          const uint32_t (&cb)[4]) {
+// The 8 fp16 weights lane half kq feeds to MFMA g of 32-value block h of the
+// stage: values 16g + 8kq + p of the block.  Q2_0 (block h is half h of the
+// 64-value block): field 2h + g of code bytes 8kq + p.  NL4 block h: nibble g
+// of code bytes 8kq + p.
+template <int WTYPE, int H, int G>
+__device__ __forceinline__ v8h decode_ops(const WRaw &w, uint32_t thi, uint32_t tlo, const uint32_t (&cb)[4]) {
     uint32_t r[4];
     if constexpr (WTYPE == 1) {
-        const int sh = 2 * (2 * h + (kg >> 1));
+        constexpr int sh = 2 * (2 * H + G);
         q2_to_f16((w.c0.x >> sh) & 0x03030303u, thi, tlo, r[0], r[1]);
         q2_to_f16((w.c0.y >> sh) & 0x03030303u, thi, tlo, r[2], r[3]);
     } else {
-        const uint2 c = h == 0 ? w.c0 : w.c1;
-        const int sh = 4 * (kg >> 1);
+        const uint2 c = H == 0 ? w.c0 : w.c1;
+        constexpr int sh = 4 * G;
         i8x4_to_f16(nl4_lookup((c.x >> sh) & 0x0F0F0F0Fu, cb), r[0], r[1]);
         i8x4_to_f16(nl4_lookup((c.y >> sh) & 0x0F0F0F0Fu, cb), r[2], r[3]);
     }
@@ -180,23 +188,13 @@ __device__ __forceinline__ v8h decode_ops(const WRaw &w, int h, int kg, uint32_t
 // The fp16 table {-2d, -d, 0, d} of a Q2_0 block scale, split into low and
 // high bytes (code c selects byte c of tlo and byte c of thi).
 __device__ __forceinline__ void q2_table(uint32_t hb, uint32_t &thi, uint32_t &tlo) {
-    _Float16 d;
-    const uint16_t hb16 = uint16_t(hb);
-    __builtin_memcpy(&d, &hb16, 2);
-    const _Float16 d2 = d * (_Float16)2.0f;   // exact unless it overflows binary16
-    uint16_t b2;
-    __builtin_memcpy(&b2, &d2, 2);
-    const uint32_t m2 = b2 ^ 0x8000u, m1 = hb ^ 0x8000u, p1 = hb;
-    tlo = (m2 & 0xFFu) | ((m1 & 0xFFu) << 8) | ((p1 & 0xFFu) << 24);
-    thi = (m2 >> 8) | ((m1 >> 8) << 8) | ((p1 >> 8) << 24);
-}
-
-__device__ __forceinline__ ARaw load_acts(const uint8_t *row, int cols, int kb) {
-    ARaw a;
-    a.q0 = *reinterpret_cast<const uint4 *>(row + 32 * kb);
-    a.q1 = *reinterpret_cast<const uint4 *>(row + 32 * kb + 16);
-    a.d = reinterpret_cast<const float *>(row + cols)[kb];
-    return a;
+    const uint32_t d = hb & 0xFFFFu;
+    // {d, 2d}: the doubling is exact unless it overflows binary16
+    const v2h two = {(_Float16)1.0f, (_Float16)2.0f};
+    const uint32_t pos = as_u32(as_v2h(d | (d << 16)) * two);
+    const uint32_t neg = pos ^ 0x80008000u;                  // {-d, -2d}
+    tlo = perm(neg, pos, 0x000C0406u);
+    thi = perm(neg, pos, 0x010C0507u);
 }
 
 // Convert one staged activation block to fp16 and store it in LDS.
@@ -222,14 +220,62 @@ __device__ __forceinline__ void static_for(F &&f) {
 
 struct Lds {
     uint8_t act[2][kMaxRows * kARow];   // staged fp16 activations, double buffered
-    float dx[2][2][kMaxRows];           // their block scales
-    float dw[kWaves][2][4][16];         // NL4: block scales of each wave's weight rows
+    float dx[2][kMaxRows][2];           // their block scales (two blocks per stage)
+    float dw[kWaves][2][2][32];         // NL4: block scales of each wave's weight rows
 };
 
-typedef float v4f __attribute__((ext_vector_type(4)));
+// One 32-value block h of a stage for Q2_0 outputs, software pipelined: the
+// MFMA pairs of (activation tile r, weight tile t) run in order n = 2r + t,
+// and the epilogue of pair n-1 is split between the two MFMAs of pair n, so
+// the vector ALU works on one result while the matrix unit computes the
+// next.  Scheduling barriers keep that order.
+template <int NA>
+__device__ __forceinline__ void block_q2_pipelined(v16f (&acc)[2][NA], const v8h (&wop)[2][2],
+                                                   const uint8_t *arow0, const float *dxrow0, int h) {
+    v8h b0 = *reinterpret_cast<const v8h *>(arow0);
+    v8h b1 = *reinterpret_cast<const v8h *>(arow0 + 32);
+    float dx = dxrow0[h];
+    v16f prev;
+    float pdx = 0.0f;
+    static_for<0, 2 * NA>([&](auto NN) {
+        constexpr int n = decltype(NN)::value;
+        constexpr int r = n >> 1, t = n & 1;
+        constexpr int pr = (n - 1) >> 1, pt = (n - 1) & 1;
+        constexpr bool next = t == 1 && r + 1 < NA;     // last use of this row tile's operands
+        v16f p = __builtin_amdgcn_mfma_f32_32x32x16_f16(wop[t][0], b0, v16f{}, 0, 0, 0);
+        if constexpr (next) b0 = *reinterpret_cast<const v8h *>(arow0 + (r + 1) * 32 * kARow);
+        if constexpr (n > 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[pt][pr][i] = __builtin_fmaf(pdx, prev[i], acc[pt][pr][i]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, next ? 1 : 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, n > 0 ? 8 : 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        p = __builtin_amdgcn_mfma_f32_32x32x16_f16(wop[t][1], b1, p, 0, 0, 0);
+        const float cdx = dx;
+        if constexpr (next) {
+            b1 = *reinterpret_cast<const v8h *>(arow0 + (r + 1) * 32 * kARow + 32);
+            dx = dxrow0[(r + 1) * 32 * 2 + h];
+        }
+        if constexpr (n > 0) {
+#pragma unroll
+            for (int i = 8; i < 16; ++i) acc[pt][pr][i] = __builtin_fmaf(pdx, prev[i], acc[pt][pr][i]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, next ? 2 : 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, n > 0 ? 8 : 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        prev = p;
+        pdx = cdx;
+    });
+    constexpr int lr = NA - 1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[1][lr][i] = __builtin_fmaf(pdx, prev[i], acc[1][lr][i]);
+}
 
-// The whole K loop of one work item.  Each wave owns 64 weight rows (four
-// 16-row tiles) and runs them against NA 16-row activation tiles (the chunk's
+// The whole K loop of one work item.  Each wave owns 64 weight rows (two
+// 32-row tiles) and runs them against NA 32-row activation tiles (the chunk's
 // rows rounded up; rows past the chunk are never stored).
 template <int WTYPE, bool DOTS, int NA>
 __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int expert, int row0,
@@ -237,24 +283,27 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    const int kg = lane >> 4;                    // k group of the MFMA operands
-    const int col = lane & 15;
+    const int kq = lane >> 5;                    // k half of the MFMA operands
+    const int col = lane & 31;
     const int cols = a.cols;
     const int nb32 = cols >> 5;
-    const size_t arb = size_t(cols) + size_t(nb32) * 8;
+    const uint32_t arb = uint32_t(cols) + uint32_t(nb32) * 8u;
     constexpr int WB = WTYPE == 1 ? 64 : 32;
     const int nbw = cols / WB;
     const int n_stages = (cols + kKS - 1) / kKS;
-    const int last_k = (n_stages - 1) * kKS;
 
-    // weights: this lane's row in each of the wave's four tiles (clamped for loads)
+    // weights: this lane's row in each of the wave's two tiles (clamped for loads)
     const uint8_t *wexp = a.w_base + a.w_off[expert];
     const uint16_t *wscales = reinterpret_cast<const uint16_t *>(wexp + size_t(a.out_rows) * nbw * 16);
     const int nw = n0 + 64 * wave;
     const bool wave_on = nw < a.out_rows;
-    int wr[4];
+    uint32_t coff[2], soff[2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) wr[t] = min(nw + 16 * t + col, a.out_rows - 1);
+    for (int t = 0; t < 2; ++t) {
+        const uint32_t wr = uint32_t(min(nw + 32 * t + col, a.out_rows - 1));
+        soff[t] = wr * uint32_t(nbw);
+        coff[t] = soff[t] * 16u + 8u * uint32_t(kq);
+    }
     uint32_t cb[4] = {0u, 0u, 0u, 0u};
     if constexpr (WTYPE == 2) {
 #pragma unroll
@@ -264,41 +313,55 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
                     (uint32_t(uint8_t(a.codebook[4 * i + 3])) << 24);
     }
     auto wload = [&](int stage, int t) {
-        return load_weights<WTYPE>(wexp, wscales, wr[t], nbw, min(stage * kKS, last_k), kg);
+        const int s = min(stage, n_stages - 1);
+        const int blk = s * (kKS / WB);                      // first block of the stage
+        const bool second = WTYPE == 2 && blk + 1 < nbw;
+        return load_weights<WTYPE>(wexp + size_t(blk) * 16, wscales + blk, coff[t], soff[t], second);
     };
 
     // activations: thread tid stages row tid/2 (clamped), block tid&1 of a stage
     const int srow = tid >> 1;
     const int sblk = tid & 1;
-    const uint8_t *sact = a.act + size_t(row0 + min(srow, nrows - 1)) * arb;
+    const uint8_t *abase = a.act + size_t(row0) * arb;
+    const uint32_t aoff = uint32_t(min(srow, nrows - 1)) * arb;
     auto aload = [&](int stage) {
-        const int kb = min(stage * kKS, last_k) / 32 + sblk;
-        return load_acts(sact, cols, min(kb, nb32 - 1));
+        const int kb = min(min(stage, n_stages - 1) * 2 + sblk, nb32 - 1);
+        ARaw r;
+        r.q0 = *reinterpret_cast<const uint4 *>(abase + aoff + 32u * kb);
+        r.q1 = *reinterpret_cast<const uint4 *>(abase + aoff + 32u * kb + 16u);
+        r.d = *reinterpret_cast<const float *>(abase + aoff + uint32_t(cols) + 4u * kb);
+        return r;
     };
 
-    v4f acc[4][NA];
+    v16f acc[2][NA];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < NA; ++r) acc[t][r] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int r = 0; r < NA; ++r)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[t][r][i] = 0.0f;
 
     // U register slots; the stage loop is unrolled by U so every slot is a
     // fixed register set.  The weights of stage x sit in wslot[x % U] and are
     // loaded U stages before use; the activations of stage x sit in
     // aslot[x % U], loaded U-1 stages before they are staged into LDS.  Each
     // stage issues its activation load before its weight load (vmcnt retires
-    // loads in order).  Fewer activation tiles leave registers for a deeper
-    // prefetch.
-    constexpr int U = NA >= 8 ? 2 : (NA >= 4 ? 3 : (NA >= 2 ? 4 : 6));
-    WRaw wslot[U][4];
+    // loads in order).  Loads and staging run in every unrolled stage, past
+    // the end too (clamped, never used), so that every path through the loop
+    // has the same loads in flight and the compiler's waits stay exact; only
+    // the compute is skipped.  Fewer activation tiles leave registers for a
+    // deeper prefetch.
+    constexpr bool PIPE = WTYPE == 1 && !DOTS;
+    constexpr int U = NA >= 3 ? 2 : (NA >= 2 ? 4 : 6);
+    WRaw wslot[U][2];
     ARaw aslot[U];
 #pragma unroll
     for (int x = 0; x < U; ++x) {
         aslot[x] = aload(x);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) wslot[x][t] = wload(x, t);
+        for (int t = 0; t < 2; ++t) wslot[x][t] = wload(x, t);
     }
-    stage_acts(aslot[0], &L.act[0][srow * kARow + 64 * sblk], &L.dx[0][sblk][srow]);
+    stage_acts(aslot[0], &L.act[0][srow * kARow + 64 * sblk], &L.dx[0][srow][sblk]);
     __syncthreads();
 
     auto stage = [&](auto J, int s) {
@@ -308,17 +371,20 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
         const int k0 = s * kKS;
         const int nv = min(kKS, cols - k0);
         const int nblk = WTYPE == 1 ? 2 : (nv >> 5);
+        // slot j's activations were staged at the end of the previous stage
+        // (or before the loop), so it takes the load of stage s + U now
+        aslot[j] = aload(s + U);
 
-        if (wave_on) {
-            uint32_t thi[4] = {0u, 0u, 0u, 0u}, tlo[4] = {0u, 0u, 0u, 0u};
+        if (wave_on && s < n_stages) {
+            uint32_t thi[2] = {0u, 0u}, tlo[2] = {0u, 0u};
             if constexpr (WTYPE == 1) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) q2_table(DOTS ? 0x3C00u : (wslot[j][t].s & 0xFFFFu), thi[t], tlo[t]);
+                for (int t = 0; t < 2; ++t) q2_table(DOTS ? 0x3C00u : wslot[j][t].s, thi[t], tlo[t]);
             } else {
                 // publish this lane's row scales for the epilogue
-                if (kg == 0) {
+                if (kq == 0) {
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
+                    for (int t = 0; t < 2; ++t) {
                         L.dw[wave][0][t][col] = half_bits_to_float(wslot[j][t].s & 0xFFFFu);
                         L.dw[wave][1][t][col] = half_bits_to_float(wslot[j][t].s >> 16);
                     }
@@ -326,80 +392,86 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
                 __builtin_amdgcn_wave_barrier();
             }
             const uint8_t *abuf = L.act[par];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            static_for<0, 2>([&](auto HH) {
+                constexpr int h = decltype(HH)::value;
                 if (h < nblk) {
-                    v8h wop[4];
+                    v8h wop[2][2];
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) wop[t] = decode_ops<WTYPE>(wslot[j][t], h, kg, thi[t], tlo[t], cb);
-                    v4f dwv[4];
+                    for (int t = 0; t < 2; ++t) {
+                        wop[t][0] = decode_ops<WTYPE, h, 0>(wslot[j][t], thi[t], tlo[t], cb);
+                        wop[t][1] = decode_ops<WTYPE, h, 1>(wslot[j][t], thi[t], tlo[t], cb);
+                    }
+                    if constexpr (PIPE) {
+                        block_q2_pipelined<NA>(acc, wop, abuf + col * kARow + (32 * h + 8 * kq) * 2,
+                                               &L.dx[par][col][0], h);
+                        return;
+                    }
+                    v4f dwv[2][4];
                     if constexpr (WTYPE == 2) {
 #pragma unroll
-                        for (int t = 0; t < 4; ++t)
-                            dwv[t] = *reinterpret_cast<const v4f *>(&L.dw[wave][h][t][4 * kg]);
+                        for (int t = 0; t < 2; ++t)
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                dwv[t][q] = *reinterpret_cast<const v4f *>(&L.dw[wave][h][t][8 * q + 4 * kq]);
                     }
 #pragma unroll
                     for (int r = 0; r < NA; ++r) {
-                        const uint8_t *src = abuf + (r * 16 + col) * kARow + (32 * h + 8 * kg) * 2;
-                        const v8h bop = *reinterpret_cast<const v8h *>(src);
-                        const float dx = L.dx[par][h][r * 16 + col];
-                        v4f d[4];
+                        const uint8_t *src = abuf + (r * 32 + col) * kARow + (32 * h + 8 * kq) * 2;
+                        const v8h b0 = *reinterpret_cast<const v8h *>(src);
+                        const v8h b1 = *reinterpret_cast<const v8h *>(src + 32);
+                        const float dx = L.dx[par][r * 32 + col][h];
 #pragma unroll
-                        for (int t = 0; t < 4; ++t)
-                            d[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wop[t], bop, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-                        if constexpr (DOTS) {
-                            const int arow = r * 16 + col;
-                            const int rr = row0 + arow - a.dots_row_begin;
-                            if (arow < nrows && rr >= 0 && rr < a.dots_n_rows) {
+                        for (int t = 0; t < 2; ++t) {
+                            v16f p = __builtin_amdgcn_mfma_f32_32x32x16_f16(wop[t][0], b0, v16f{}, 0, 0, 0);
+                            p = __builtin_amdgcn_mfma_f32_32x32x16_f16(wop[t][1], b1, p, 0, 0, 0);
+                            if constexpr (DOTS) {
+                                const int arow = r * 32 + col;
+                                const int rr = row0 + arow - a.dots_row_begin;
+                                if (arow < nrows && rr >= 0 && rr < a.dots_n_rows) {
 #pragma unroll
-                                for (int t = 0; t < 4; ++t)
+                                    for (int i = 0; i < 16; ++i) {
+                                        const int wrow = nw + 32 * t + 8 * (i >> 2) + 4 * kq + (i & 3);
+                                        a.dots[(size_t(rr) * a.out_rows + wrow) * nb32 + (k0 >> 5) + h] = int(p[i]);
+                                    }
+                                }
+                            } else if constexpr (WTYPE == 1) {
 #pragma unroll
-                                    for (int v = 0; v < 4; ++v)
-                                        a.dots[(size_t(rr) * a.out_rows + nw + 16 * t + 4 * kg + v) * nb32 + (k0 >> 5) + h] =
-                                            int(d[t][v]);
+                                for (int i = 0; i < 16; ++i) acc[t][r][i] = __builtin_fmaf(dx, p[i], acc[t][r][i]);
+                            } else {
+#pragma unroll
+                                for (int i = 0; i < 16; ++i)
+                                    acc[t][r][i] = __builtin_fmaf(dx, dwv[t][i >> 2][i & 3] * p[i], acc[t][r][i]);
                             }
-                        } else if constexpr (WTYPE == 1) {
-#pragma unroll
-                            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                                for (int v = 0; v < 4; ++v) acc[t][r][v] = __builtin_fmaf(dx, d[t][v], acc[t][r][v]);
-                        } else {
-#pragma unroll
-                            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                                for (int v = 0; v < 4; ++v)
-                                    acc[t][r][v] = __builtin_fmaf(dx, dwv[t][v] * d[t][v], acc[t][r][v]);
                         }
                     }
                 }
-            }
+            });
         }
 
-        if (s + 1 < n_stages)
-            stage_acts(aslot[jn], &L.act[par ^ 1][srow * kARow + 64 * sblk], &L.dx[par ^ 1][sblk][srow]);
-        aslot[j] = aload(s + U);
+        stage_acts(aslot[jn], &L.act[par ^ 1][srow * kARow + 64 * sblk], &L.dx[par ^ 1][srow][sblk]);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) wslot[j][t] = wload(s + U, t);
+        for (int t = 0; t < 2; ++t) wslot[j][t] = wload(s + U, t);
         __syncthreads();
     };
 
     for (int s0 = 0; s0 < n_stages; s0 += U)
-        static_for<0, U>([&](auto J) {
-            const int s = s0 + decltype(J)::value;
-            if (s < n_stages) stage(J, s);
-        });
+        static_for<0, U>([&](auto J) { stage(J, s0 + decltype(J)::value); });
 
     if constexpr (!DOTS) {
         if (!wave_on) return;
 #pragma unroll
         for (int r = 0; r < NA; ++r) {
-            const int arow = r * 16 + col;
+            const int arow = r * 32 + col;
             if (arow >= nrows) continue;
             const int rr = row0 + arow;
             const size_t orow = a.perm ? size_t(a.perm[rr]) : size_t(rr);
-            float *dst = a.out + orow * a.out_rows + nw + 4 * kg;
+            float *dst = a.out + orow * a.out_rows + nw + 4 * kq;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) *reinterpret_cast<v4f *>(dst + 16 * t) = acc[t][r];
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<v4f *>(dst + 32 * t + 8 * q) =
+                        v4f{acc[t][r][4 * q], acc[t][r][4 * q + 1], acc[t][r][4 * q + 2], acc[t][r][4 * q + 3]};
         }
     }
 }
@@ -421,15 +493,15 @@ __global__ __launch_bounds__(256, 2) void expert_product_kernel(ProductArgs a) {
     const int nrows = a.chunks[4 * c + 2];
     const int n0 = tile * kTileRows;
 
-    const int na = (nrows + 15) >> 4;          // 16-row activation tiles: 1..8
+    const int na = (nrows + 31) >> 5;          // 32-row activation tiles: 1..4
     if (na <= 1)
         run_item<WTYPE, DOTS, 1>(a, L, expert, row0, nrows, n0);
-    else if (na <= 2)
+    else if (na == 2)
         run_item<WTYPE, DOTS, 2>(a, L, expert, row0, nrows, n0);
-    else if (na <= 4)
-        run_item<WTYPE, DOTS, 4>(a, L, expert, row0, nrows, n0);
+    else if (na == 3)
+        run_item<WTYPE, DOTS, 3>(a, L, expert, row0, nrows, n0);
     else
-        run_item<WTYPE, DOTS, 8>(a, L, expert, row0, nrows, n0);
+        run_item<WTYPE, DOTS, 4>(a, L, expert, row0, nrows, n0);
 }
 
 hipError_t launch_expert_product(const ProductArgs &a, hipStream_t stream) {
