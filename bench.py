@@ -30,9 +30,10 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 # the products run on fp16 matrix cores (int8 values and 2/4-bit weights are
 # exact in fp16): dense fp16 MFMA peak
 MFMA_F16_PEAK_TFLOPS = 2500.0
-# fp32 FMA on the vector ALU without packed instructions:
-# 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz
-VALU_F32_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+# fp32 FMA on the vector ALU: 256 CU x 4 SIMD x 32 lanes per clock x 2 flop x
+# 2.4 GHz = 157.3 TFLOP/s.  A wave64 v_fmac_f32 on VGPR operands issues every
+# ~2.3 clocks on gfx950 (measured), so this rate needs no packed instructions.
+VALU_F32_PEAK_TFLOPS = 256 * 4 * 32 * 2 * 2.4e9 / 1e12
 KERNELS = ["quantize_scatter", "expert_gate_up", "swiglu_q8", "expert_down"]
 KERNEL_SOURCES = {
     "expert_gate_up": "quantized_moe_expert_scatter_amd/csrc/expert_kernels.hip",
@@ -124,7 +125,9 @@ def run_cpu_baseline(L, threads, target_rows):
                           n_threads=threads)
     dt = time.perf_counter() - t0
     ms_layer = dt * 1e3 * cfg.rows / rows.size
-    return {"value": round(ms_layer, 1), "unit": "ms/layer", "cores": threads, "kind": "oracle",
+    useful_ops = 2 * cfg.rows * (2 * cfg.n_ff * cfg.hidden + cfg.hidden * cfg.n_ff)
+    return {"value": round(useful_ops / (ms_layer * 1e-3) / 1e12, 4), "unit": "effective int8 TOPS",
+            "ms_per_layer": round(ms_layer, 1), "cores": threads, "kind": "oracle",
             "sample": f"{rows.size} of {cfg.rows} expert-sorted rows (all rows of experts "
                       f"0..{n_e - 1}) of the {cfg.name} layer, full chain, {dt:.1f} s wall, "
                       f"scaled by rows"}

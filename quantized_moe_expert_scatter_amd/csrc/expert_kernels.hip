@@ -224,26 +224,44 @@ struct Lds {
     float dw[kWaves][2][2][32];         // NL4: block scales of each wave's weight rows
 };
 
-// One 32-value block h of a stage for Q2_0 outputs, software pipelined: the
-// MFMA pairs of (activation tile r, weight tile t) run in order n = 2r + t,
-// and the epilogue of pair n-1 is split between the two MFMAs of pair n, so
-// the vector ALU works on one result while the matrix unit computes the
-// next.  Scheduling barriers keep that order.
+// One stage (two 32-value blocks h) of Q2_0 outputs, software pipelined as
+// one stream of MFMA pairs n = (h, r, t) (activation tile r, weight tile t):
+// the epilogue of pair n-1 is split between the two MFMAs of pair n, so the
+// vector ALU works on one result while the matrix unit computes the next;
+// each activation operand is read from LDS right after its last use by the
+// previous row tile; the second block's weights are decoded into the
+// registers of the first as soon as those are dead, inside the stream.
+// Scheduling barriers keep that order.
 template <int NA>
-__device__ __forceinline__ void block_q2_pipelined(v16f (&acc)[2][NA], const v8h (&wop)[2][2],
-                                                   const uint8_t *arow0, const float *dxrow0, int h) {
+__device__ __forceinline__ void stage_q2_pipelined(v16f (&acc)[2][NA], const WRaw (&w)[2], const uint32_t (&thi)[2],
+                                                   const uint32_t (&tlo)[2], const uint8_t *arow0,
+                                                   const float *dxrow0) {
+    constexpr int NP = 4 * NA;                    // pairs in the stage
+    const uint32_t cb[4] = {0u, 0u, 0u, 0u};
+    // operands of the first row tile of block 0, then the decode of block 0
     v8h b0 = *reinterpret_cast<const v8h *>(arow0);
     v8h b1 = *reinterpret_cast<const v8h *>(arow0 + 32);
-    float dx = dxrow0[h];
+    float dx = dxrow0[0];
+    v8h wop[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        wop[t][0] = decode_ops<1, 0, 0>(w[t], thi[t], tlo[t], cb);
+        wop[t][1] = decode_ops<1, 0, 1>(w[t], thi[t], tlo[t], cb);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     v16f prev;
     float pdx = 0.0f;
-    static_for<0, 2 * NA>([&](auto NN) {
+    static_for<0, NP>([&](auto NN) {
         constexpr int n = decltype(NN)::value;
-        constexpr int r = n >> 1, t = n & 1;
-        constexpr int pr = (n - 1) >> 1, pt = (n - 1) & 1;
-        constexpr bool next = t == 1 && r + 1 < NA;     // last use of this row tile's operands
+        constexpr int h = n / (2 * NA), r = (n >> 1) % NA, t = n & 1;
+        constexpr int pr = ((n - 1) >> 1) % NA, pt = (n - 1) & 1;
+        // the operands that follow this row tile: (h, r+1) or (1, 0)
+        constexpr bool next = t == 1 && (r + 1 < NA || h == 0);
+        constexpr int nh = r + 1 < NA ? h : 1, nr = r + 1 < NA ? r + 1 : 0;
+        const uint8_t *nsrc = arow0 + nr * 32 * kARow + 64 * nh;
+        // segment A: first MFMA of the pair, next b0, first half of the previous epilogue
         v16f p = __builtin_amdgcn_mfma_f32_32x32x16_f16(wop[t][0], b0, v16f{}, 0, 0, 0);
-        if constexpr (next) b0 = *reinterpret_cast<const v8h *>(arow0 + (r + 1) * 32 * kARow);
+        if constexpr (next) b0 = *reinterpret_cast<const v8h *>(nsrc);
         if constexpr (n > 0) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) acc[pt][pr][i] = __builtin_fmaf(pdx, prev[i], acc[pt][pr][i]);
@@ -252,11 +270,12 @@ __device__ __forceinline__ void block_q2_pipelined(v16f (&acc)[2][NA], const v8h
         __builtin_amdgcn_sched_group_barrier(0x100, next ? 1 : 0, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, n > 0 ? 8 : 0, 0);
         __builtin_amdgcn_sched_barrier(0);
+        // segment B: second MFMA, next b1 and dx, second half of the previous epilogue
         p = __builtin_amdgcn_mfma_f32_32x32x16_f16(wop[t][1], b1, p, 0, 0, 0);
         const float cdx = dx;
         if constexpr (next) {
-            b1 = *reinterpret_cast<const v8h *>(arow0 + (r + 1) * 32 * kARow + 32);
-            dx = dxrow0[(r + 1) * 32 * 2 + h];
+            b1 = *reinterpret_cast<const v8h *>(nsrc + 32);
+            dx = dxrow0[nr * 32 * 2 + nh];
         }
         if constexpr (n > 0) {
 #pragma unroll
@@ -266,6 +285,12 @@ __device__ __forceinline__ void block_q2_pipelined(v16f (&acc)[2][NA], const v8h
         __builtin_amdgcn_sched_group_barrier(0x100, next ? 2 : 0, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, n > 0 ? 8 : 0, 0);
         __builtin_amdgcn_sched_barrier(0);
+        // block 1's weights of tile t once block 0's last pair of tile t has issued
+        if constexpr (h == 0 && r == NA - 1) {
+            wop[t][0] = decode_ops<1, 1, 0>(w[t], thi[t], tlo[t], cb);
+            wop[t][1] = decode_ops<1, 1, 1>(w[t], thi[t], tlo[t], cb);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         prev = p;
         pdx = cdx;
     });
@@ -392,7 +417,10 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
                 __builtin_amdgcn_wave_barrier();
             }
             const uint8_t *abuf = L.act[par];
-            static_for<0, 2>([&](auto HH) {
+            if constexpr (PIPE) {
+                stage_q2_pipelined<NA>(acc, wslot[j], thi, tlo, abuf + col * kARow + 16 * kq,
+                                       &L.dx[par][col][0]);
+            } else static_for<0, 2>([&](auto HH) {
                 constexpr int h = decltype(HH)::value;
                 if (h < nblk) {
                     v8h wop[2][2];
@@ -400,11 +428,6 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
                     for (int t = 0; t < 2; ++t) {
                         wop[t][0] = decode_ops<WTYPE, h, 0>(wslot[j][t], thi[t], tlo[t], cb);
                         wop[t][1] = decode_ops<WTYPE, h, 1>(wslot[j][t], thi[t], tlo[t], cb);
-                    }
-                    if constexpr (PIPE) {
-                        block_q2_pipelined<NA>(acc, wop, abuf + col * kARow + (32 * h + 8 * kq) * 2,
-                                               &L.dx[par][col][0], h);
-                        return;
                     }
                     v4f dwv[2][4];
                     if constexpr (WTYPE == 2) {
