@@ -34,8 +34,12 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 # 2.4 GHz = 157.3 TFLOP/s.  A wave64 v_fmac_f32 on VGPR operands issues every
 # ~2.3 clocks on gfx950 (measured), so this rate needs no packed instructions.
 VALU_F32_PEAK_TFLOPS = 256 * 4 * 32 * 2 * 2.4e9 / 1e12
-KERNELS = ["quantize_scatter", "expert_gate_up", "swiglu_q8", "expert_down"]
+# the timed step: the whole path in three launches (gate/up, swiglu and q8_1
+# fused); the four-launch form with GU in memory is reported alongside
+KERNELS = ["quantize_scatter", "expert_gate_up_swiglu_q8", "expert_down"]
+KERNELS_4 = ["quantize_scatter", "expert_gate_up", "swiglu_q8", "expert_down"]
 KERNEL_SOURCES = {
+    "expert_gate_up_swiglu_q8": "quantized_moe_expert_scatter_amd/csrc/expert_kernels.hip",
     "expert_gate_up": "quantized_moe_expert_scatter_amd/csrc/expert_kernels.hip",
     "expert_down": "quantized_moe_expert_scatter_amd/csrc/expert_kernels.hip",
     "quantize_scatter": "quantized_moe_expert_scatter_amd/csrc/quant_kernels.hip",
@@ -57,24 +61,31 @@ def algorithmic(cfg, counts):
         "quantize_scatter": T * H * 4 + R * q8(H),
         "expert_gate_up": R * q8(H) + w_gu + R * 2 * F * 4,
         "swiglu_q8": R * 2 * F * 4 + R * q8(F),
+        "expert_gate_up_swiglu_q8": R * q8(H) + w_gu + R * q8(F),
         "expert_down": R * q8(F) + w_dn + R * H * 4,
     }
-    ops = {"expert_gate_up": 2 * R * 2 * F * H, "expert_down": 2 * R * H * F}
+    ops = {"expert_gate_up": 2 * R * 2 * F * H, "expert_gate_up_swiglu_q8": 2 * R * 2 * F * H,
+           "expert_down": 2 * R * H * F}
     # epilogue: one fp32 FMA (2 flop) per (row, output, 32-value block) for
     # Q2_0 (d*dot comes out of the MFMA), two for NL4 (d*dot, then the FMA)
     dn_epi = 2 if cfg.down_type == 1 else 4
-    alu = {"expert_gate_up": 2 * R * 2 * F * (H // 32), "expert_down": dn_epi * R * H * (F // 32)}
+    alu = {"expert_gate_up": 2 * R * 2 * F * (H // 32), "expert_gate_up_swiglu_q8": 2 * R * 2 * F * (H // 32),
+           "expert_down": dn_epi * R * H * (F // 32)}
     return by, ops, alu
 
 
-def time_layer(D, steps, warmup):
+def time_layer(D, steps, warmup, fused=True):
     import torch
     stream = torch.cuda.current_stream()
-    fns = [D.quantize_scatter, D.expert_gate_up, D.swiglu_q8, D.expert_down]
+    if fused:
+        names, fns = KERNELS, [D.quantize_scatter, D.expert_gate_up_swiglu_q8, D.expert_down]
+    else:
+        names, fns = KERNELS_4, [D.quantize_scatter, D.expert_gate_up, D.swiglu_q8, D.expert_down]
     for _ in range(warmup):
-        D.run()
+        for f in fns:
+            f()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -88,7 +99,7 @@ def time_layer(D, steps, warmup):
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     per_kernel = {k: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]))
-                  for i, k in enumerate(KERNELS)}
+                  for i, k in enumerate(names)}
     return total_ms / steps, per_kernel
 
 
@@ -169,12 +180,16 @@ def main():
         counts = D.plan.query()[0]
         steps = args.steps if name == args.workload else max(5, args.steps // 5)
         ms, per_kernel = time_layer(D, steps, args.warmup)
+        ms4, per_kernel4 = time_layer(D, max(3, steps // 5), 1, fused=False)
         by, ops, alu = algorithmic(cfg, counts)
         useful_ops = ops["expert_gate_up"] + ops["expert_down"]
+        step_bytes = sum(by[k] for k in KERNELS)
         results[name] = {"ms_per_layer": round(ms, 4), "tops": round(useful_ops / (ms * 1e-3) / 1e12, 1),
                          "per_kernel_ms": {k: round(v, 4) for k, v in per_kernel.items()},
-                         "algorithmic_bytes": int(sum(by.values())),
-                         "hbm_floor_ms": round(sum(by.values()) / (HBM_PEAK_GBS * 1e9) * 1e3, 4),
+                         "algorithmic_bytes": int(step_bytes),
+                         "hbm_floor_ms": round(step_bytes / (HBM_PEAK_GBS * 1e9) * 1e3, 4),
+                         "four_launch": {"ms_per_layer": round(ms4, 4),
+                                         "per_kernel_ms": {k: round(v, 4) for k, v in per_kernel4.items()}},
                          "steps": steps, "setup_s": round(setup_s, 2)}
         print(f"[bench] {name}: {ms:.3f} ms/layer {results[name]['tops']} TOPS {per_kernel}",
               file=sys.stderr, flush=True)
@@ -227,7 +242,8 @@ def main():
                    "tokens": main_cfg.tokens, "rows": main_cfg.rows, "chunk_rows": args.chunk_rows},
         "per_kernel_ms": m["per_kernel_ms"],
         "hbm_floor_ms": m["hbm_floor_ms"],
-        "layers": {k: {kk: v[kk] for kk in ("ms_per_layer", "tops", "per_kernel_ms", "hbm_floor_ms")}
+        "layers": {k: {kk: v[kk] for kk in ("ms_per_layer", "tops", "per_kernel_ms", "hbm_floor_ms",
+                                            "four_launch")}
                    for k, v in results.items()},
         "roofline": roof,
         "cpu_baseline": cpu,

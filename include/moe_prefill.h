@@ -10,6 +10,7 @@
  *   quantize_scatter   X (fp32) -> q8_1 rows, one copy per (token, expert)
  *   expert_gate_up     q8_1 rows x Q2_0 gate/up weights -> GU (fp32)
  *   swiglu_q8          GU -> q8_1 of silu(gate) * up, H never stored as floats
+ *   expert_gate_up_swiglu_q8   the two above in one launch, GU never stored
  *   expert_down        q8_1 H rows x down weights -> one fp32 row per (token, expert)
  *
  * Conventions shared by every entry point:
@@ -169,6 +170,14 @@ int expert_gate_up(const moe_plan *plan, const void *xq, float *gu, void *stream
  * gu: device fp32 [tokens*topk x 2*n_ff]; hq: device
  * moe_q8_1_bytes(tokens*topk, n_ff) bytes; both 16-byte aligned. */
 int swiglu_q8(const moe_plan *plan, const float *gu, void *hq, void *stream);
+
+/* Steps 2 and 3 in one launch: the gate/up product of step 2 with the
+ * swiglu and q8_1 of step 3 applied to its fp32 results in registers, so GU
+ * never reaches memory (the same fusion PR #3752 makes for swiglu_quant, one
+ * step earlier).  hq is byte for byte what expert_gate_up followed by
+ * swiglu_q8 writes.  xq: device q8_1 rows [tokens*topk x hidden]; hq: device
+ * moe_q8_1_bytes(tokens*topk, n_ff) bytes; both 16-byte aligned. */
+int expert_gate_up_swiglu_q8(const moe_plan *plan, const void *xq, void *hq, void *stream);
 
 /* Step 4 ("Strata" PR #3752: the down product as one launch into one row per
  * (token, expert), the K loop stopping at n_ff).

@@ -24,7 +24,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EALIGN", -3: "MOE_EFORMAT",
 # every symbol include/moe_prefill.h declares
 EXPORTS = ["moe_q8_1_bytes", "moe_weight_bytes", "moe_plan_device_bytes", "moe_prefill_plan",
            "moe_plan_query", "moe_plan_destroy", "quantize_scatter", "expert_gate_up",
-           "swiglu_q8", "expert_down", "moe_debug_block_dots", "moe_status_string"]
+           "swiglu_q8", "expert_gate_up_swiglu_q8", "expert_down", "moe_debug_block_dots",
+           "moe_status_string"]
 
 
 class MoeError(RuntimeError):
@@ -65,7 +66,8 @@ def lib() -> ctypes.CDLL:
         L.moe_plan_query.restype = I
         L.moe_plan_destroy.argtypes = [P]
         L.moe_plan_destroy.restype = None
-        for name in ("quantize_scatter", "expert_gate_up", "swiglu_q8", "expert_down"):
+        for name in ("quantize_scatter", "expert_gate_up", "swiglu_q8", "expert_gate_up_swiglu_q8",
+                     "expert_down"):
             f = getattr(L, name)
             f.argtypes = [P, P, P, P]
             f.restype = I
@@ -195,6 +197,11 @@ def expert_gate_up(plan: Plan, xq, gu, stream=None):
 
 def swiglu_q8(plan: Plan, gu, hq, stream=None):
     _check(lib().swiglu_q8(plan.handle, _ptr(gu), _ptr(hq), _stream(stream)), "swiglu_q8")
+
+
+def expert_gate_up_swiglu_q8(plan: Plan, xq, hq, stream=None):
+    _check(lib().expert_gate_up_swiglu_q8(plan.handle, _ptr(xq), _ptr(hq), _stream(stream)),
+           "expert_gate_up_swiglu_q8")
 
 
 def expert_down(plan: Plan, hq, dm, stream=None):

@@ -52,6 +52,7 @@
 //    chunks of an expert land on one XCD, so its weight tiles and activation
 //    rows are re-read from that XCD's L2.
 #include "internal.h"
+#include "q8_1.cuh"
 
 #include <hip/hip_runtime.h>
 
@@ -299,12 +300,55 @@ __device__ __forceinline__ void stage_q2_pipelined(v16f (&acc)[2][NA], const WRa
     for (int i = 0; i < 16; ++i) acc[1][lr][i] = __builtin_fmaf(pdx, prev[i], acc[1][lr][i]);
 }
 
+constexpr int kOut = 0;     // fp32 outputs
+constexpr int kDots = 1;    // the int32 block dots (test export)
+constexpr int kSwiglu = 2;  // gate/up with swiglu and q8_1 of H in the epilogue
+
+// Fused epilogue for one activation row: the lane holds gate (tile 0) and up
+// (tile 1) of the same 16 j's, h = silu(g) * u exactly as swiglu_q8 computes
+// it, and the 32-value q8_1 block of h is shared with lane ^ 32.
+__device__ __forceinline__ void swiglu_store_row(const v16f &g, const v16f &u, uint8_t *hrow, int n_ff,
+                                                 int jbase, int kq) {
+    float h[16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float e = static_cast<float>(exp(-static_cast<double>(g[i])));
+        h[i] = g[i] / (1.0f + e) * u[i];
+        amax = __builtin_fmaxf(amax, __builtin_fabsf(h[i]));
+    }
+    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
+    const float d = amax / 127.0f;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    int32_t sum = 0;
+    if (d != 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int8_t q = q8_round(h[i], d);
+            sum += q;
+            w[i >> 2] |= uint32_t(uint8_t(q)) << (8 * (i & 3));
+        }
+    }
+    sum += __shfl_xor(sum, 32);
+    // value i of the lane is j = jbase + 8 (i / 4) + 4 kq + i % 4
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<uint32_t *>(hrow + jbase + 8 * q + 4 * kq) = w[q];
+    if (kq == 0) {
+        const int blk = jbase >> 5;
+        reinterpret_cast<float *>(hrow + n_ff)[blk] = d;
+        reinterpret_cast<int32_t *>(hrow + n_ff + 4 * (n_ff >> 5))[blk] = sum;
+    }
+}
+
 // The whole K loop of one work item.  Each wave owns 64 weight rows (two
 // 32-row tiles) and runs them against NA 32-row activation tiles (the chunk's
-// rows rounded up; rows past the chunk are never stored).
-template <int WTYPE, bool DOTS, int NA>
+// rows rounded up; rows past the chunk are never stored).  In the fused
+// swiglu mode the item's tile is 128 j's: the wave's tile 0 is gate rows
+// j0..j0+31 and its tile 1 the up rows n_ff+j0..n_ff+j0+31 of the same j's.
+template <int WTYPE, int MODE, int NA>
 __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int expert, int row0,
                                          int nrows, int n0) {
+    constexpr bool DOTS = MODE == kDots;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
@@ -320,12 +364,15 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
     // weights: this lane's row in each of the wave's two tiles (clamped for loads)
     const uint8_t *wexp = a.w_base + a.w_off[expert];
     const uint16_t *wscales = reinterpret_cast<const uint16_t *>(wexp + size_t(a.out_rows) * nbw * 16);
-    const int nw = n0 + 64 * wave;
-    const bool wave_on = nw < a.out_rows;
+    const int n_ff = a.out_rows >> 1;
+    const int nw = MODE == kSwiglu ? n0 + 32 * wave : n0 + 64 * wave;
+    const bool wave_on = nw < (MODE == kSwiglu ? n_ff : a.out_rows);
+    // first weight row of each of the wave's two tiles
+    const int tb[2] = {nw, MODE == kSwiglu ? n_ff + nw : nw + 32};
     uint32_t coff[2], soff[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        const uint32_t wr = uint32_t(min(nw + 32 * t + col, a.out_rows - 1));
+        const uint32_t wr = uint32_t(min(tb[t] + col, a.out_rows - 1));
         soff[t] = wr * uint32_t(nbw);
         coff[t] = soff[t] * 16u + 8u * uint32_t(kq);
     }
@@ -480,7 +527,18 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
     for (int s0 = 0; s0 < n_stages; s0 += U)
         static_for<0, U>([&](auto J) { stage(J, s0 + decltype(J)::value); });
 
-    if constexpr (!DOTS) {
+    if constexpr (MODE == kSwiglu) {
+        if (!wave_on) return;
+        const size_t hrb = size_t(n_ff) + size_t(n_ff >> 5) * 8;
+#pragma unroll
+        for (int r = 0; r < NA; ++r) {
+            // lanes l and l ^ 32 hold the two halves of a block and share the
+            // activation row, so they skip rows past the chunk together
+            const int arow = r * 32 + col;
+            if (arow < nrows)
+                swiglu_store_row(acc[0][r], acc[1][r], a.hq + size_t(row0 + arow) * hrb, n_ff, nw, kq);
+        }
+    } else if constexpr (!DOTS) {
         if (!wave_on) return;
 #pragma unroll
         for (int r = 0; r < NA; ++r) {
@@ -499,7 +557,7 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
     }
 }
 
-template <int WTYPE, bool DOTS>
+template <int WTYPE, int MODE>
 __global__ __launch_bounds__(256, 2) void expert_product_kernel(ProductArgs a) {
     __shared__ __attribute__((aligned(16))) Lds L;
 
@@ -514,17 +572,17 @@ __global__ __launch_bounds__(256, 2) void expert_product_kernel(ProductArgs a) {
     const int expert = a.chunks[4 * c + 0];
     const int row0 = a.chunks[4 * c + 1];
     const int nrows = a.chunks[4 * c + 2];
-    const int n0 = tile * kTileRows;
+    const int n0 = tile * (MODE == kSwiglu ? kTileRows / 2 : kTileRows);
 
     const int na = (nrows + 31) >> 5;          // 32-row activation tiles: 1..4
     if (na <= 1)
-        run_item<WTYPE, DOTS, 1>(a, L, expert, row0, nrows, n0);
+        run_item<WTYPE, MODE, 1>(a, L, expert, row0, nrows, n0);
     else if (na == 2)
-        run_item<WTYPE, DOTS, 2>(a, L, expert, row0, nrows, n0);
+        run_item<WTYPE, MODE, 2>(a, L, expert, row0, nrows, n0);
     else if (na == 3)
-        run_item<WTYPE, DOTS, 3>(a, L, expert, row0, nrows, n0);
+        run_item<WTYPE, MODE, 3>(a, L, expert, row0, nrows, n0);
     else
-        run_item<WTYPE, DOTS, 4>(a, L, expert, row0, nrows, n0);
+        run_item<WTYPE, MODE, 4>(a, L, expert, row0, nrows, n0);
 }
 
 hipError_t launch_expert_product(const ProductArgs &a, hipStream_t stream) {
@@ -532,14 +590,16 @@ hipError_t launch_expert_product(const ProductArgs &a, hipStream_t stream) {
     const dim3 grid(kXcds * a.max_items), block(64 * kWaves);
     if (a.wtype == 1) {
         if (a.dots)
-            hipLaunchKernelGGL((expert_product_kernel<1, true>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((expert_product_kernel<1, kDots>), grid, block, 0, stream, a);
+        else if (a.hq)
+            hipLaunchKernelGGL((expert_product_kernel<1, kSwiglu>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((expert_product_kernel<1, false>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((expert_product_kernel<1, kOut>), grid, block, 0, stream, a);
     } else {
         if (a.dots)
-            hipLaunchKernelGGL((expert_product_kernel<2, true>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((expert_product_kernel<2, kDots>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((expert_product_kernel<2, false>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((expert_product_kernel<2, kOut>), grid, block, 0, stream, a);
     }
     return hipGetLastError();
 }

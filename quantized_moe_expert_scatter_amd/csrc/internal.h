@@ -55,6 +55,7 @@ struct ProductArgs {
     const int32_t *xcd;        // device: per-XCD list starts and counts
     const int32_t *perm;       // device: sorted row -> output row (NULL: identity)
     float *out;                // fp32 outputs
+    uint8_t *hq;               // gate/up fused with swiglu: q8_1 rows of H (else NULL)
     int32_t *dots;             // debug: int32 block dots instead of outputs
     int wtype;                 // 1 Q2_0, 2 NL4
     int cols;                  // contraction length

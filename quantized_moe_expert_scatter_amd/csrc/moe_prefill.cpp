@@ -291,6 +291,20 @@ int expert_gate_up(const moe_plan *p, const void *xq, float *gu, void *stream) {
     return hip_status(launch_expert_product(a, static_cast<hipStream_t>(stream)));
 }
 
+int expert_gate_up_swiglu_q8(const moe_plan *p, const void *xq, void *hq, void *stream) {
+    int st = ready(p);
+    if (st) return st;
+    if (p->rows == 0) return MOE_OK;
+    if (!xq || !hq) return MOE_EINVAL;
+    if (!aligned16(xq) || !aligned16(hq)) return MOE_EALIGN;
+    ProductArgs a = product_args(p, 0, xq);
+    // work items of 128 j's: gate rows j and up rows n_ff + j together
+    a.n_tiles = (p->n_ff + kTileRows / 2 - 1) / (kTileRows / 2);
+    a.max_items = p->max_xcd_chunks * a.n_tiles;
+    a.hq = static_cast<uint8_t *>(hq);
+    return hip_status(launch_expert_product(a, static_cast<hipStream_t>(stream)));
+}
+
 int swiglu_q8(const moe_plan *p, const float *gu, void *hq, void *stream) {
     int st = ready(p);
     if (st) return st;

@@ -65,13 +65,24 @@ class DeviceLayer:
     def swiglu_q8(self, stream=None):
         _lib.swiglu_q8(self.plan, self.gu, self.hq, stream)
 
+    def expert_gate_up_swiglu_q8(self, stream=None):
+        _lib.expert_gate_up_swiglu_q8(self.plan, self.xq, self.hq, stream)
+
     def expert_down(self, stream=None):
         _lib.expert_down(self.plan, self.hq, self.dm, stream)
 
     def run(self, stream=None):
+        """The four steps, one launch each (GU materialised)."""
         self.quantize_scatter(stream)
         self.expert_gate_up(stream)
         self.swiglu_q8(stream)
+        self.expert_down(stream)
+
+    def run_fused(self, stream=None):
+        """The same layer with gate/up, swiglu and q8_1 in one launch (GU never
+        stored): three launches, the same xq, hq and dm bytes."""
+        self.quantize_scatter(stream)
+        self.expert_gate_up_swiglu_q8(stream)
         self.expert_down(stream)
 
     # host copies

@@ -28,7 +28,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     L = _lib.lib()
     decl = declared_functions()
-    assert len(decl) >= 12
+    assert len(decl) >= 13
     for name in decl:
         assert hasattr(L, name), name
     assert sorted(decl) == sorted(_lib.EXPORTS)
@@ -161,8 +161,10 @@ def test_host_only_plan_refuses_kernels():
     ids = wl.routing_uniform(8, 4, 2, seed=1)
     plan = _lib.moe_prefill_plan(ids, 4, 64, *_weights(cfg))
     L = _lib.lib()
-    for f in (L.quantize_scatter, L.expert_gate_up, L.swiglu_q8, L.expert_down):
+    for f in (L.quantize_scatter, L.expert_gate_up, L.swiglu_q8, L.expert_gate_up_swiglu_q8,
+              L.expert_down):
         assert f(plan.handle, FAKE_BASE, FAKE_BASE, None) == -6
+        assert f(None, FAKE_BASE, FAKE_BASE, None) == -1
     assert L.moe_debug_block_dots(plan.handle, 0, FAKE_BASE, 0, 1, FAKE_BASE, None) == -6
     assert L.quantize_scatter(None, FAKE_BASE, FAKE_BASE, None) == -1
     with pytest.raises(_lib.MoeError):

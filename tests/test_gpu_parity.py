@@ -181,6 +181,31 @@ def test_zero_and_huge_token_rows():
     D.close()
 
 
+def _fused_equals_two_steps(D):
+    """Run the layer both ways on the same buffers; hq and dm must match byte
+    for byte (compared on the device)."""
+    D.run()
+    torch.cuda.synchronize()
+    hq_a, dm_a = D.hq.clone(), D.dm.clone()
+    D.hq.fill_(0x5A)
+    D.dm.fill_(float("nan"))
+    D.run_fused()
+    torch.cuda.synchronize()
+    assert torch.equal(D.hq, hq_a), "fused hq differs from gate_up + swiglu_q8"
+    assert torch.equal(D.dm.view(torch.int32), dm_a.view(torch.int32)), "dm after the fused path differs"
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_fused_gate_up_swiglu_matches_two_steps(name):
+    """expert_gate_up_swiglu_q8 writes the bytes of expert_gate_up followed by
+    swiglu_q8, including n_ff not a multiple of its 128-value tile."""
+    L = _small_layer(name)
+    _say("case", name)
+    D = device_layer(L)
+    _fused_equals_two_steps(D)
+    D.close()
+
+
 # ------------------------------------------------------------- full layers
 FULL = ["2k", "8k", "16k", "t128"]
 
@@ -191,7 +216,7 @@ def test_full_layer_sampled_rows(name):
     _say("case", name, "generating inputs")
     L = wl.make_layer(cfg)
     pl = oracle.plan(L.ids, cfg.n_expert, 64)
-    D = device_layer(L)
+    D = device_layer(L, chunk_rows=128)          # the benchmark's launch configuration
     D.run()
     torch.cuda.synchronize()
     _say("device run done")
@@ -222,4 +247,7 @@ def test_full_layer_sampled_rows(name):
     for t in range(4):
         rs = tok_rows[t * cfg.topk:(t + 1) * cfg.topk]
         assert all(np.array_equal(xq_dev[rs[0]], xq_dev[r]) for r in rs)
+    # the fused gate/up + swiglu launch the benchmark times: same bytes, whole layer
+    _fused_equals_two_steps(D)
+    _say("fused path equal")
     D.close()
