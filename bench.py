@@ -144,16 +144,54 @@ def run_cpu_baseline(L, threads, target_rows):
                       f"scaled by rows"}
 
 
+def run_sweep(args, wl, DeviceLayer, torch):
+    """ms/layer and effective TOPS over the sweep's layers, three- and
+    four-launch forms, with rows per expert and chunks per launch."""
+    out = {}
+    for name, cfg in wl.SWEEP.items():
+        print(f"[sweep] {name}: generating inputs", file=sys.stderr, flush=True)
+        L = wl.make_layer(cfg)
+        D = DeviceLayer(L.x, L.ids, L.w_gu, L.w_down, chunk_rows=args.chunk_rows)
+        torch.cuda.synchronize()
+        counts, _, _, chunks = D.plan.query()
+        n_chunks = chunks.shape[0]
+        steps = max(5, args.steps // 2)
+        ms, pk = time_layer(D, steps, args.warmup)
+        ms4, pk4 = time_layer(D, steps, args.warmup, fused=False)
+        _, ops, _ = algorithmic(cfg, counts)
+        useful = ops["expert_gate_up"] + ops["expert_down"]
+        used = counts[counts > 0]
+        out[name] = {"tokens": cfg.tokens, "routing": cfg.routing if cfg.routing != "lognormal"
+                     else f"lognormal sigma {cfg.sigma}",
+                     "experts_used": int(used.size), "rows_per_expert_median": float(np.median(used)),
+                     "rows_per_expert_max": int(used.max()), "chunks": int(n_chunks),
+                     "ms_per_layer": round(ms, 4), "tops": round(useful / (ms * 1e-3) / 1e12, 1),
+                     "per_kernel_ms": {k: round(v, 4) for k, v in pk.items()},
+                     "four_launch_ms": round(ms4, 4),
+                     "four_launch_per_kernel_ms": {k: round(v, 4) for k, v in pk4.items()}}
+        print(f"[sweep] {name}: {ms:.3f} ms (four-launch {ms4:.3f}) {out[name]['tops']} TOPS",
+              file=sys.stderr, flush=True)
+        D.close()
+        del D
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "ms/layer over the rows-per-expert sweep", "unit": "ms",
+                      "n_gpus": 1, "chunk_rows": args.chunk_rows, "layers": out}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="16k", choices=["tiny", "2k", "8k", "16k", "t128"])
+    ap.add_argument("--workload", default="16k",
+                    help="tiny | 2k | 8k | 16k | t128, or a sweep layer sw<T>_<ln0.5|ln1.0|flat32>")
     ap.add_argument("--also", default="2k,8k,t128", help="other layers reported alongside")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=6000)
     ap.add_argument("--chunk-rows", type=int, default=128)
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead: the rows-per-expert sweep (768..4096 tokens x lognormal "
+                         "sigma 0.5 / 1.0 and flat 32-row routing), one JSON line of ms/layer")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -165,12 +203,16 @@ def main():
 
     assert torch.cuda.is_available(), "bench needs the GPU"
     torch.cuda.set_device(0)
+    if args.sweep:
+        run_sweep(args, wl, DeviceLayer, torch)
+        return
+    layers = {**wl.CONFIGS, **wl.SWEEP}
     results = {}
-    main_cfg = wl.CONFIGS[args.workload]
+    main_cfg = layers[args.workload]
     names = [args.workload] + [n for n in args.also.split(",") if n and n != args.workload]
     main_layer = None
     for name in names:
-        cfg = wl.CONFIGS[name]
+        cfg = layers[name]
         print(f"[bench] {name}: generating inputs", file=sys.stderr, flush=True)
         L = wl.make_layer(cfg)
         t0 = time.perf_counter()

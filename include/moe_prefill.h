@@ -6,6 +6,7 @@
  * experts": commit list and Approach; PR #2145 "fused int8 prompt experts on
  * Turing": description):
  *
+ *   moe_weights_pack   (once per layer, at load) weights -> the kernels' tiled layout
  *   moe_prefill_plan   routing ids -> expert-sorted rows, offsets, chunk table
  *   quantize_scatter   X (fp32) -> q8_1 rows, one copy per (token, expert)
  *   expert_gate_up     q8_1 rows x Q2_0 gate/up weights -> GU (fp32)
@@ -44,6 +45,11 @@
  *       codes plane: 16-byte blocks of 32 values, value b in the low nibble of
  *         byte b, value 16+b in the high nibble; weight = d*codebook[code]
  *       scales plane: binary16 d per 32-value block.
+ *   Tiled layout (MOE_W_TILED, what the product kernels read; written by
+ *   moe_weights_pack): the same two planes with the same sizes, each in
+ *   (row tile, block, row in tile) order for 32-row tiles -- block b of row
+ *   32*i + r sits at slot (i * blocks_per_row + b) * 32 + r of its plane, so
+ *   the 32 rows of one block are 512 contiguous code bytes and 64 scale bytes.
  *   Expert outputs are fp32.  The per-32-value epilogue is, for each output,
  *       acc = 0; for each 32-value block b in K order:
  *         acc = fmaf(dx_b, dw_b * (float)dot_b, acc)
@@ -71,13 +77,14 @@ typedef enum {
     MOE_ESTATE = -6    /* the plan was built without a device workspace */
 } moe_status;
 
-typedef enum { MOE_W_Q2_0 = 1, MOE_W_NL4 = 2 } moe_wtype;
+typedef enum { MOE_W_Q2_0 = 1, MOE_W_NL4 = 2, MOE_W_TILED = 0x100 } moe_wtype;
 
 /* The weights of one product (gate/up or down) for all experts of a layer,
  * read in place: expert e's matrix starts at base + offset[e] ("Strata"
  * PR #3752, commit list: a per-layer offset table from the expert cache's
  * base, uploaded with the group bounds).
- *   type      MOE_W_Q2_0, or MOE_W_NL4 (down product only)
+ *   type      MOE_W_Q2_0, or MOE_W_NL4 (down product only); the plan takes
+ *             weights in the tiled layout, type | MOE_W_TILED
  *   rows      output features (gate/up: 2*n_ff; down: hidden), % 64 == 0
  *   cols      contraction length (gate/up: hidden; down: n_ff), % 64 (Q2_0)
  *             or % 32 (NL4) == 0
@@ -105,8 +112,22 @@ typedef struct moe_plan moe_plan;  /* opaque host object */
  * Returns 0 if cols % 32 != 0 or a size is negative. */
 size_t moe_q8_1_bytes(int rows, int cols);
 
-/* Bytes of one expert's matrix in the given format (0 on a bad format/dim). */
+/* Bytes of one expert's matrix in the given format, either layout (0 on a
+ * bad format/dim). */
 size_t moe_weight_bytes(int type, int rows, int cols);
+
+/* Write the tiled layout of every expert of `w` (row-major planes, type
+ * MOE_W_Q2_0 or MOE_W_NL4 without MOE_W_TILED) into dst: expert e's tiled
+ * matrix at dst + w->offset[e], the same offsets and sizes as the source, so
+ * the descriptor {type | MOE_W_TILED, ..., base = dst, base_bytes =
+ * dst_bytes, same offsets} then describes the packed weights.  A pure byte
+ * permutation inside each plane, done once when a layer is loaded (one launch
+ * when the experts sit at a constant stride, else one per expert).
+ *   dst        device buffer, 16-byte aligned, every expert inside dst_bytes,
+ *              not overlapping w->base's buffer; owned by the caller.
+ * Experts must share a matrix (equal offsets) or not overlap.  Asynchronous
+ * on `stream`; the source must stay valid until the copy has run. */
+int moe_weights_pack(const moe_weights *w, void *dst, size_t dst_bytes, void *stream);
 
 /* Device workspace the plan needs for T tokens, top-k, n_expert experts and
  * chunks of at most chunk_rows rows (sorted-row maps, expert offsets, the
@@ -124,6 +145,7 @@ size_t moe_plan_device_bytes(int tokens, int topk, int n_expert, int chunk_rows)
  *              workgroup processes one chunk against 256 weight rows).
  *   w_gu       gate/up weights: Q2_0, rows = 2*n_ff, cols = hidden.
  *   w_down     down weights: Q2_0 or NL4, rows = hidden, cols = n_ff.
+ *              Both in the tiled layout (type | MOE_W_TILED), else MOE_EFORMAT.
  *   plan_dev   device workspace of moe_plan_device_bytes(...) bytes, 16-byte
  *              aligned, owned by the caller, not touched by anything else
  *              while the plan lives; NULL builds a host-only plan (for

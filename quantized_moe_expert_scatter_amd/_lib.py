@@ -17,12 +17,14 @@ LIB_PATH = os.path.join(HERE, "libmoe_prefill.so")
 
 MOE_W_Q2_0 = 1
 MOE_W_NL4 = 2
+MOE_W_TILED = 0x100
 
 STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EALIGN", -3: "MOE_EFORMAT",
           -4: "MOE_ESIZE", -5: "MOE_EHIP", -6: "MOE_ESTATE"}
 
 # every symbol include/moe_prefill.h declares
-EXPORTS = ["moe_q8_1_bytes", "moe_weight_bytes", "moe_plan_device_bytes", "moe_prefill_plan",
+EXPORTS = ["moe_q8_1_bytes", "moe_weight_bytes", "moe_weights_pack", "moe_plan_device_bytes",
+           "moe_prefill_plan",
            "moe_plan_query", "moe_plan_destroy", "quantize_scatter", "expert_gate_up",
            "swiglu_q8", "expert_gate_up_swiglu_q8", "expert_down", "moe_debug_block_dots",
            "moe_status_string"]
@@ -57,6 +59,8 @@ def lib() -> ctypes.CDLL:
         L.moe_q8_1_bytes.restype = Z
         L.moe_weight_bytes.argtypes = [I, I, I]
         L.moe_weight_bytes.restype = Z
+        L.moe_weights_pack.argtypes = [ctypes.POINTER(moe_weights), P, Z, P]
+        L.moe_weights_pack.restype = I
         L.moe_plan_device_bytes.argtypes = [I, I, I, I]
         L.moe_plan_device_bytes.restype = Z
         L.moe_prefill_plan.argtypes = [P, I, I, I, I, ctypes.POINTER(moe_weights),
@@ -132,6 +136,17 @@ class Weights:
             wtype, rows, cols, n_expert, base_ptr, base_bytes,
             self.offsets.ctypes.data if self.offsets.size else None,
             None if self.codebook is None else self.codebook.ctypes.data)
+
+
+def moe_weights_pack(w: Weights, dst, stream=None) -> Weights:
+    """Writes the tiled layout of w (row-major planes) into the device tensor
+    dst and returns the descriptor of the packed weights (same offsets)."""
+    nbytes = dst.numel() * dst.element_size()
+    _check(lib().moe_weights_pack(ctypes.byref(w.struct), _ptr(dst), nbytes, _stream(stream)),
+           "moe_weights_pack")
+    s = w.struct
+    return Weights(s.type | MOE_W_TILED, s.rows, s.cols, s.n_expert, dst, nbytes, w.offsets,
+                   w.codebook)
 
 
 class Plan:

@@ -158,10 +158,11 @@ __device__ __forceinline__ WRaw load_weights(const uint8_t *codes, const uint16_
         w.s = scales[soff];
     } else {
         // the second block of a half-filled last stage is clamped to the first
-        const uint32_t o1 = second ? 16u : 0u;
+        // the next block of the same 32 rows is 32 slots further
+        const uint32_t o1 = second ? 32u : 0u;
         w.c0 = *reinterpret_cast<const uint2 *>(codes + coff);
-        w.c1 = *reinterpret_cast<const uint2 *>(codes + coff + o1);
-        w.s = uint32_t(scales[soff]) | (uint32_t(scales[soff + (o1 >> 4)]) << 16);
+        w.c1 = *reinterpret_cast<const uint2 *>(codes + coff + 16u * o1);
+        w.s = uint32_t(scales[soff]) | (uint32_t(scales[soff + o1]) << 16);
     }
     return w;
 }
@@ -361,7 +362,8 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
     const int nbw = cols / WB;
     const int n_stages = (cols + kKS - 1) / kKS;
 
-    // weights: this lane's row in each of the wave's two tiles (clamped for loads)
+    // weights (tiled layout: block b of row 32i + r at slot (i * nbw + b) * 32 + r):
+    // this lane's row in each of the wave's two tiles (clamped for loads)
     const uint8_t *wexp = a.w_base + a.w_off[expert];
     const uint16_t *wscales = reinterpret_cast<const uint16_t *>(wexp + size_t(a.out_rows) * nbw * 16);
     const int n_ff = a.out_rows >> 1;
@@ -373,7 +375,7 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const uint32_t wr = uint32_t(min(tb[t] + col, a.out_rows - 1));
-        soff[t] = wr * uint32_t(nbw);
+        soff[t] = (wr & ~31u) * uint32_t(nbw) + (wr & 31u);      // slot of block 0
         coff[t] = soff[t] * 16u + 8u * uint32_t(kq);
     }
     uint32_t cb[4] = {0u, 0u, 0u, 0u};
@@ -388,7 +390,7 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
         const int s = min(stage, n_stages - 1);
         const int blk = s * (kKS / WB);                      // first block of the stage
         const bool second = WTYPE == 2 && blk + 1 < nbw;
-        return load_weights<WTYPE>(wexp + size_t(blk) * 16, wscales + blk, coff[t], soff[t], second);
+        return load_weights<WTYPE>(wexp + size_t(blk) * 512, wscales + 32 * blk, coff[t], soff[t], second);
     };
 
     // activations: thread tid stages row tid/2 (clamped), block tid&1 of a stage
@@ -427,11 +429,16 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
     constexpr int U = NA >= 3 ? 2 : (NA >= 2 ? 4 : 6);
     WRaw wslot[U][2];
     ARaw aslot[U];
+    // the prologue issues the slots' loads in the loop's own order (the
+    // scheduler would otherwise group them by base address): the waits at the
+    // loop head merge this path with the back edge, so any load that trails
+    // here shortens the prefetch of every iteration
 #pragma unroll
     for (int x = 0; x < U; ++x) {
         aslot[x] = aload(x);
 #pragma unroll
         for (int t = 0; t < 2; ++t) wslot[x][t] = wload(x, t);
+        __builtin_amdgcn_sched_barrier(0);
     }
     stage_acts(aslot[0], &L.act[0][srow * kARow + 64 * sblk], &L.dx[0][srow][sblk]);
     __syncthreads();

@@ -38,7 +38,13 @@ namespace {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int block_values(int type) { return type == MOE_W_Q2_0 ? 64 : (type == MOE_W_NL4 ? 32 : 0); }
+// the block format of a weight type, with or without the MOE_W_TILED flag
+int base_type(int type) { return type & ~int(MOE_W_TILED); }
+
+int block_values(int type) {
+    const int t = base_type(type);
+    return t == MOE_W_Q2_0 ? 64 : (t == MOE_W_NL4 ? 32 : 0);
+}
 
 size_t weight_bytes(int type, int rows, int cols) {
     const int blk = block_values(type);
@@ -46,14 +52,18 @@ size_t weight_bytes(int type, int rows, int cols) {
     return size_t(rows) * size_t(cols / blk) * 18u;
 }
 
-int check_weights(const moe_weights *w, int n_expert, bool allow_nl4) {
+// Shape, alignment and extent of a weight descriptor.  `tiled`: the layout
+// flag the caller must (1) or must not (0) have set.
+int check_weights(const moe_weights *w, int n_expert, bool allow_nl4, bool tiled) {
     if (!w || !w->base || !w->offset) return MOE_EINVAL;
-    if (w->type != MOE_W_Q2_0 && !(allow_nl4 && w->type == MOE_W_NL4)) return MOE_EFORMAT;
+    const int t = base_type(w->type);
+    if (t != MOE_W_Q2_0 && !(allow_nl4 && t == MOE_W_NL4)) return MOE_EFORMAT;
+    if (((w->type & MOE_W_TILED) != 0) != tiled) return MOE_EFORMAT;
     if (w->n_expert != n_expert || w->rows <= 0 || w->cols <= 0) return MOE_EINVAL;
-    if (w->rows % 64 || w->cols % block_values(w->type)) return MOE_EFORMAT;
-    if (w->type == MOE_W_NL4 && !w->codebook) return MOE_EINVAL;
+    if (w->rows % 64 || w->cols % block_values(t)) return MOE_EFORMAT;
+    if (t == MOE_W_NL4 && !w->codebook) return MOE_EINVAL;
     if (!aligned16(w->base)) return MOE_EALIGN;
-    const size_t per = weight_bytes(w->type, w->rows, w->cols);
+    const size_t per = weight_bytes(t, w->rows, w->cols);
     for (int e = 0; e < n_expert; ++e) {
         if (w->offset[e] & 15u) return MOE_EALIGN;
         if (w->offset[e] > w->base_bytes || w->base_bytes - w->offset[e] < per) return MOE_ESIZE;
@@ -73,6 +83,42 @@ size_t moe_q8_1_bytes(int rows, int cols) {
 }
 
 size_t moe_weight_bytes(int type, int rows, int cols) { return weight_bytes(type, rows, cols); }
+
+int moe_weights_pack(const moe_weights *w, void *dst, size_t dst_bytes, void *stream) {
+    if (!w || !dst) return MOE_EINVAL;
+    const int st = check_weights(w, w->n_expert, true, false);
+    if (st) return st;
+    if (w->n_expert <= 0) return MOE_EINVAL;
+    if (!aligned16(dst)) return MOE_EALIGN;
+    const size_t per = weight_bytes(w->type, w->rows, w->cols);
+    for (int e = 0; e < w->n_expert; ++e)
+        if (w->offset[e] > dst_bytes || dst_bytes - w->offset[e] < per) return MOE_ESIZE;
+    // experts either share a matrix (equal offsets) or do not overlap
+    std::vector<uint64_t> offs(w->offset, w->offset + w->n_expert);
+    std::sort(offs.begin(), offs.end());
+    for (size_t i = 1; i < offs.size(); ++i)
+        if (offs[i] != offs[i - 1] && offs[i] - offs[i - 1] < per) return MOE_EINVAL;
+    // the copy gathers: source and destination must not overlap
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(w->base), d0 = reinterpret_cast<uintptr_t>(dst);
+    if (s0 < d0 + dst_bytes && d0 < s0 + w->base_bytes) return MOE_EINVAL;
+    const auto *src = static_cast<const uint8_t *>(w->base);
+    auto *out = static_cast<uint8_t *>(dst);
+    const int nb = w->cols / block_values(w->type);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    // experts at a constant stride go in one launch, others one launch each
+    bool uniform = w->n_expert <= 65535;
+    const uint64_t stride = w->n_expert > 1 ? w->offset[1] - w->offset[0] : 0;
+    for (int e = 1; uniform && e < w->n_expert; ++e)
+        uniform = w->offset[e] >= w->offset[0] && w->offset[e] - w->offset[0] == uint64_t(e) * stride;
+    if (uniform)
+        return hip_status(launch_weight_pack(src + w->offset[0], out + w->offset[0], stride,
+                                             stride ? w->n_expert : 1, w->rows, nb, s));
+    for (int e = 0; e < w->n_expert; ++e) {
+        const hipError_t err = launch_weight_pack(src + w->offset[e], out + w->offset[e], 0, 1, w->rows, nb, s);
+        if (err != hipSuccess) return MOE_EHIP;
+    }
+    return MOE_OK;
+}
 
 size_t moe_plan_device_bytes(int tokens, int topk, int n_expert, int chunk_rows) {
     if (tokens < 0 || topk <= 0 || n_expert <= 0 || chunk_rows <= 0 || chunk_rows > kMaxChunkRows)
@@ -103,9 +149,9 @@ int moe_prefill_plan(const int32_t *ids, int tokens, int topk, int n_expert, int
     if (tokens > 0 && !ids) return MOE_EINVAL;
     const long long R64 = (long long)tokens * topk;
     if (R64 > (1LL << 30)) return MOE_EINVAL;
-    int st = check_weights(w_gu, n_expert, false);
+    int st = check_weights(w_gu, n_expert, false, true);
     if (st) return st;
-    st = check_weights(w_down, n_expert, true);
+    st = check_weights(w_down, n_expert, true, true);
     if (st) return st;
     if (w_gu->rows % 2 || w_down->rows != w_gu->cols || w_down->cols * 2 != w_gu->rows)
         return MOE_EINVAL;
@@ -125,7 +171,7 @@ int moe_prefill_plan(const int32_t *ids, int tokens, int topk, int n_expert, int
     p->gu = *w_gu; p->dn = *w_down;
     p->gu_off.assign(w_gu->offset, w_gu->offset + n_expert);
     p->dn_off.assign(w_down->offset, w_down->offset + n_expert);
-    if (w_down->type == MOE_W_NL4) std::memcpy(p->dn_codebook, w_down->codebook, 16);
+    if (base_type(w_down->type) == MOE_W_NL4) std::memcpy(p->dn_codebook, w_down->codebook, 16);
     p->gu.offset = p->gu_off.data();
     p->dn.offset = p->dn_off.data();
     p->dn.codebook = p->dn_codebook;
@@ -271,12 +317,12 @@ static ProductArgs product_args(const moe_plan *p, int product, const void *act)
     a.chunks = reinterpret_cast<const int32_t *>(dev_at(p, p->layout.chunks));
     a.xcd = reinterpret_cast<const int32_t *>(dev_at(p, p->layout.xcd));
     a.perm = product == 0 ? nullptr : reinterpret_cast<const int32_t *>(dev_at(p, p->layout.perm));
-    a.wtype = w.type;
+    a.wtype = base_type(w.type);
     a.cols = w.cols;
     a.out_rows = w.rows;
     a.n_tiles = (w.rows + kTileRows - 1) / kTileRows;
     a.max_items = p->max_xcd_chunks * a.n_tiles;
-    if (w.type == MOE_W_NL4) std::memcpy(a.codebook, p->dn_codebook, 16);
+    if (a.wtype == MOE_W_NL4) std::memcpy(a.codebook, p->dn_codebook, 16);
     return a;
 }
 

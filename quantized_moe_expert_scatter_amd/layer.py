@@ -19,7 +19,8 @@ def _to_device(a: np.ndarray, device):
 class DeviceLayer:
     """Uploads one layer's weights and inputs, owns every buffer of the path.
 
-    x: float32 [T, hidden]; ids: int32 [T, topk]; w_gu / w_down: ExpertWeights.
+    x: float32 [T, hidden]; ids: int32 [T, topk]; w_gu / w_down: ExpertWeights
+    (row-major planes; packed here into the kernels' tiled layout).
     Buffers: xq (q8_1 rows of hidden), gu (fp32 [R, 2*n_ff]), hq (q8_1 rows of
     n_ff), dm (fp32 [T*topk, hidden]); R = T*topk.
     """
@@ -35,12 +36,10 @@ class DeviceLayer:
         self.rows = self.tokens * self.topk
         self.chunk_rows = chunk_rows
         self.x = _to_device(x.astype(np.float32, copy=False), self.device)
-        self.w_gu_dev = _to_device(w_gu.buf, self.device)
-        self.w_dn_dev = _to_device(w_down.buf, self.device)
-        self.w_gu = _lib.Weights(w_gu.wtype, w_gu.rows, w_gu.cols, w_gu.n_expert, self.w_gu_dev,
-                                 w_gu.buf.nbytes, w_gu.offsets)
-        self.w_dn = _lib.Weights(w_down.wtype, w_down.rows, w_down.cols, w_down.n_expert,
-                                 self.w_dn_dev, w_down.buf.nbytes, w_down.offsets, w_down.codebook)
+        # weights arrive as row-major planes and are packed once into the
+        # kernels' tiled layout; the row-major copies are dropped after that
+        self.w_gu = self._packed(w_gu, stream)
+        self.w_dn = self._packed(w_down, stream)
         u8 = torch.uint8
         ws = _lib.moe_plan_device_bytes(self.tokens, self.topk, self.n_expert, chunk_rows)
         self.workspace = torch.empty(max(ws, 16), dtype=u8, device=self.device)
@@ -54,6 +53,16 @@ class DeviceLayer:
                               device=self.device)
         self.plan = _lib.moe_prefill_plan(ids, self.n_expert, chunk_rows, self.w_gu, self.w_dn,
                                           workspace=self.workspace, stream=stream)
+
+    def _packed(self, w: ExpertWeights, stream) -> "_lib.Weights":
+        import torch
+        raw = _to_device(w.buf, self.device)
+        rw = _lib.Weights(w.wtype, w.rows, w.cols, w.n_expert, raw, w.buf.nbytes, w.offsets,
+                          w.codebook)
+        dst = torch.empty_like(raw)
+        packed = _lib.moe_weights_pack(rw, dst, stream)
+        torch.cuda.synchronize(self.device)     # the pack has read raw before it is freed
+        return packed
 
     # the four steps, each one kernel launch
     def quantize_scatter(self, stream=None):

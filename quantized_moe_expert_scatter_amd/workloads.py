@@ -63,7 +63,7 @@ class LayerConfig:
     n_ff: int
     n_expert: int
     topk: int
-    routing: str  # "uniform" | "lognormal"
+    routing: str  # "uniform" | "lognormal" | "flat32"
     down_type: int = Q2_0
     sigma: float = 1.0
     x_seed: int = 0
@@ -93,6 +93,20 @@ CONFIGS = {
     "t128": LayerConfig("t128", 128, 2560, 640, 512, 10, "uniform", down_type=NL4,
                         x_seed=51, ids_seed=52, gu_seed=_LAYER_GU_SEED, down_seed=1052),
 }
+
+
+# The rows-per-expert sweep: prompt chunks of 768..4096 tokens under skewed
+# (lognormal sigma 0.5, 1.0) and flat (32 rows per routed expert, at most 512
+# experts) routings, on the same layer as 2k / 8k / 16k.
+SWEEP_TOKENS = (768, 1024, 1536, 4096)
+SWEEP_ROUTINGS = (("ln0.5", "lognormal", 0.5), ("ln1.0", "lognormal", 1.0), ("flat32", "flat32", 1.0))
+SWEEP = {}
+for _t in SWEEP_TOKENS:
+    for _i, (_tag, _kind, _sigma) in enumerate(SWEEP_ROUTINGS):
+        _name = f"sw{_t}_{_tag}"
+        SWEEP[_name] = LayerConfig(_name, _t, 2560, 640, 512, 10, _kind, sigma=_sigma,
+                                   x_seed=6000 + 10 * _t + _i, ids_seed=7000 + 10 * _t + _i,
+                                   gu_seed=_LAYER_GU_SEED, down_seed=_LAYER_DOWN_SEED)
 
 
 def block_of(wtype: int) -> int:
@@ -139,11 +153,25 @@ def routing_lognormal(tokens: int, n_expert: int, topk: int, sigma: float, seed:
     return ids
 
 
+def routing_flat(tokens: int, n_expert: int, topk: int, per_expert: int, seed: int) -> np.ndarray:
+    """Every routed expert gets the same number of rows: the first
+    min(n_expert, tokens*topk/per_expert) experts of a seeded permutation,
+    taken round robin over the flattened (token, slot) order, so a token's
+    topk experts are distinct whenever at least topk experts are used."""
+    rng = np.random.default_rng(seed)
+    used = max(topk, min(n_expert, (tokens * topk) // per_expert))
+    experts = rng.permutation(n_expert)[:used].astype(np.int32)
+    flat = np.arange(tokens * topk, dtype=np.int64) % used
+    return experts[flat].reshape(tokens, topk)
+
+
 def routing(cfg: LayerConfig) -> np.ndarray:
     if cfg.routing == "uniform":
         return routing_uniform(cfg.tokens, cfg.n_expert, cfg.topk, cfg.ids_seed)
     if cfg.routing == "lognormal":
         return routing_lognormal(cfg.tokens, cfg.n_expert, cfg.topk, cfg.sigma, cfg.ids_seed)
+    if cfg.routing == "flat32":
+        return routing_flat(cfg.tokens, cfg.n_expert, cfg.topk, 32, cfg.ids_seed)
     raise ValueError(cfg.routing)
 
 

@@ -43,6 +43,7 @@ def test_size_queries():
     assert _lib.moe_weight_bytes(1, 2560, 640) == 460800
     assert _lib.moe_weight_bytes(1, 64, 96) == 0
     assert _lib.moe_weight_bytes(3, 64, 64) == 0
+    assert _lib.moe_weight_bytes(1 | _lib.MOE_W_TILED, 1280, 2560) == 921600
     assert _lib.moe_plan_device_bytes(64, 2, 8, 64) > 0
     assert _lib.moe_plan_device_bytes(64, 2, 8, 128) > 0
     assert _lib.moe_plan_device_bytes(64, 2, 8, 129) == 0
@@ -51,7 +52,7 @@ def test_size_queries():
         assert _lib.status_string(s)
 
 
-def _weights(cfg, base=FAKE_BASE, shuffle=False, down_type=None):
+def _weights(cfg, base=FAKE_BASE, shuffle=False, down_type=None, tiled=True):
     F, H, E = cfg.n_ff, cfg.hidden, cfg.n_expert
     dt = cfg.down_type if down_type is None else down_type
     gu_per = _lib.moe_weight_bytes(1, 2 * F, H)
@@ -60,9 +61,10 @@ def _weights(cfg, base=FAKE_BASE, shuffle=False, down_type=None):
     dn_off = np.arange(E, dtype=np.uint64) * np.uint64(dn_per)
     if shuffle:
         gu_off = gu_off[::-1].copy()
-    w_gu = _lib.Weights(1, 2 * F, H, E, base, gu_per * E, gu_off)
+    flag = _lib.MOE_W_TILED if tiled else 0
+    w_gu = _lib.Weights(1 | flag, 2 * F, H, E, base, gu_per * E, gu_off)
     cb = wl.nl4_codebook(1) if dt == 2 else None
-    w_dn = _lib.Weights(dt, H, F, E, base, dn_per * E, dn_off, cb)
+    w_dn = _lib.Weights(dt | flag, H, F, E, base, dn_per * E, dn_off, cb)
     return w_gu, w_dn
 
 
@@ -130,6 +132,10 @@ def test_validation_errors():
     w_gu, w_dn = _weights(cfg)
     w_gu.struct.type = 3
     assert _plan_status(ids, 4, 64, w_gu, w_dn) == -3
+    for which in (0, 1):                       # the kernels read only the tiled layout
+        ws = list(_weights(cfg))
+        ws[which].struct.type &= ~_lib.MOE_W_TILED
+        assert _plan_status(ids, 4, 64, *ws) == -3
     w_gu, w_dn = _weights(cfg)
     w_gu.struct.type = 2                       # NL4 gate/up is not supported
     assert _plan_status(ids, 4, 64, w_gu, w_dn) == -3
@@ -169,3 +175,38 @@ def test_host_only_plan_refuses_kernels():
     assert L.quantize_scatter(None, FAKE_BASE, FAKE_BASE, None) == -1
     with pytest.raises(_lib.MoeError):
         _lib.expert_gate_up(plan, None, None, stream=0)
+
+
+def _pack_status(w, dst, dst_bytes):
+    return _lib.lib().moe_weights_pack(ctypes.byref(w.struct) if w is not None else None, dst,
+                                       dst_bytes, None)
+
+
+def test_pack_validation_errors():
+    """moe_weights_pack refuses, before any HIP call, every descriptor and
+    destination it cannot pack."""
+    cfg = wl.small_config("v", 8, 128, 64, 4, 2)
+    DST = 1 << 36                                # another stand-in, far from FAKE_BASE
+    w_gu, w_dn = _weights(cfg, tiled=False)
+    size = w_gu.struct.base_bytes
+    assert _pack_status(None, DST, size) == -1
+    assert _pack_status(w_gu, None, size) == -1
+    assert _pack_status(w_gu, DST + 8, size) == -2
+    assert _pack_status(w_gu, DST, size - 16) == -4
+    assert _pack_status(w_gu, FAKE_BASE + 64, size) == -1      # overlaps the source
+    t_gu, _ = _weights(cfg, tiled=True)
+    assert _pack_status(t_gu, DST, size) == -3                  # already tiled
+    w_gu.struct.type = 3
+    assert _pack_status(w_gu, DST, size) == -3
+    w_gu, _ = _weights(cfg, tiled=False)
+    w_gu.struct.rows = 96                                       # not a multiple of 64
+    assert _pack_status(w_gu, DST, size) == -3
+    w_gu, _ = _weights(cfg, tiled=False)
+    w_gu.offsets[1] = w_gu.offsets[0] + np.uint64(16)           # experts overlap partly
+    assert _pack_status(w_gu, DST, size) == -1
+    w_gu, _ = _weights(cfg, tiled=False)
+    w_gu.offsets[1] += np.uint64(8)
+    assert _pack_status(w_gu, DST, size) == -2
+    _, w_dn = _weights(cfg, tiled=False, down_type=2)
+    w_dn.struct.codebook = None
+    assert _pack_status(w_dn, DST, w_dn.struct.base_bytes) == -1

@@ -212,7 +212,17 @@ FULL = ["2k", "8k", "16k", "t128"]
 
 @pytest.mark.parametrize("name", FULL)
 def test_full_layer_sampled_rows(name):
-    cfg = wl.CONFIGS[name]
+    _sampled_rows(wl.CONFIGS[name])
+
+
+@pytest.mark.parametrize("name", list(wl.SWEEP))
+def test_sweep_layer_sampled_rows(name):
+    """The rows-per-expert sweep: 768..4096 tokens, lognormal and flat routing."""
+    _sampled_rows(wl.SWEEP[name])
+
+
+def _sampled_rows(cfg):
+    name = cfg.name
     _say("case", name, "generating inputs")
     L = wl.make_layer(cfg)
     pl = oracle.plan(L.ids, cfg.n_expert, 64)

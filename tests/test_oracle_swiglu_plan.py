@@ -133,10 +133,13 @@ def check_plan_invariants(ids, E, C, counts, offsets, perm, chunks):
 
 
 @pytest.mark.parametrize("kind,T,E,K,C", [("uniform", 300, 16, 4, 8), ("lognormal", 500, 32, 6, 16),
-                                          ("uniform", 64, 8, 2, 64), ("lognormal", 2048, 512, 10, 64)])
+                                          ("uniform", 64, 8, 2, 64), ("lognormal", 2048, 512, 10, 64),
+                                          ("flat", 768, 512, 10, 16), ("flat", 4096, 512, 10, 64)])
 def test_plan_invariants(kind, T, E, K, C):
     if kind == "uniform":
         ids = wl.routing_uniform(T, E, K, seed=T)
+    elif kind == "flat":
+        ids = wl.routing_flat(T, E, K, 32, seed=T)   # many equal counts: the tie order decides
     else:
         ids = wl.routing_lognormal(T, E, K, 1.0, seed=T)
     pl = oracle.plan(ids, E, C)
@@ -155,3 +158,22 @@ def test_plan_empty_experts_and_duplicates():
     pl = oracle.plan(ids, 5, 1)
     assert pl.counts.tolist() == [1, 0, 3, 0, 0]
     assert pl.chunks[:, 0].tolist() == [2, 2, 2, 0]
+
+
+@pytest.mark.parametrize("name", list(wl.SWEEP))
+def test_sweep_routings(name):
+    """The sweep's inputs: T tokens, top-10 distinct experts per token; the
+    flat routing gives every routed expert the same row count, 32 where
+    T*10/32 experts fit in 512, else T*10/512."""
+    cfg = wl.SWEEP[name]
+    ids = wl.routing(cfg)
+    assert ids.shape == (cfg.tokens, cfg.topk)
+    assert ids.min() >= 0 and ids.max() < cfg.n_expert
+    assert all(len(set(r)) == cfg.topk for r in ids.tolist())
+    counts = np.bincount(ids.ravel(), minlength=cfg.n_expert)
+    if cfg.routing == "flat32":
+        used = counts[counts > 0]
+        assert used.size == min(cfg.n_expert, cfg.rows // 32)
+        assert used.min() == used.max() == cfg.rows // used.size
+    else:
+        assert counts.max() > 2 * np.median(counts[counts > 0])      # skewed
