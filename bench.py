@@ -54,7 +54,8 @@ def algorithmic(cfg, counts):
     R = T * K
     touched = int(np.count_nonzero(counts))
     dn_blk = 64 if cfg.down_type == 1 else 32
-    w_gu = touched * 2 * F * (H // 64) * 18
+    gu_blk = 64 if cfg.gu_type == 1 else 32
+    w_gu = touched * 2 * F * (H // gu_blk) * 18
     w_dn = touched * H * (F // dn_blk) * 18
     q8 = lambda n: n + n // 32 * 8
     by = {
@@ -69,7 +70,9 @@ def algorithmic(cfg, counts):
     # epilogue: one fp32 FMA (2 flop) per (row, output, 32-value block) for
     # Q2_0 (d*dot comes out of the MFMA), two for NL4 (d*dot, then the FMA)
     dn_epi = 2 if cfg.down_type == 1 else 4
-    alu = {"expert_gate_up": 2 * R * 2 * F * (H // 32), "expert_gate_up_swiglu_q8": 2 * R * 2 * F * (H // 32),
+    gu_epi = 2 if cfg.gu_type == 1 else 4
+    alu = {"expert_gate_up": gu_epi * R * 2 * F * (H // 32),
+           "expert_gate_up_swiglu_q8": gu_epi * R * 2 * F * (H // 32),
            "expert_down": dn_epi * R * H * (F // 32)}
     return by, ops, alu
 
@@ -129,7 +132,8 @@ def run_cpu_baseline(L, threads, target_rows):
     t0 = time.perf_counter()
     xq = oracle.quantize_scatter(L.x, cfg.topk, pl.perm, rows=rows)
     gu = oracle.expert_product(L.w_gu.wtype, L.w_gu.buf, L.w_gu.offsets, cfg.n_expert,
-                               2 * cfg.n_ff, cfg.hidden, None, xq, row_e[rows], n_threads=threads)
+                               2 * cfg.n_ff, cfg.hidden, L.w_gu.codebook, xq, row_e[rows],
+                               n_threads=threads)
     hq = oracle.swiglu_q8(gu, cfg.n_ff)
     oracle.expert_product(L.w_down.wtype, L.w_down.buf, L.w_down.offsets, cfg.n_expert,
                           cfg.hidden, cfg.n_ff, L.w_down.codebook, hq, row_e[rows],
@@ -279,7 +283,7 @@ def main():
         "data": "synthetic (seeded: X ~ N(0,1), uniform Q2_0 codes, fp16 scales U[0.01,0.05])",
         "config": {"workload": f"{main_cfg.name}: T={main_cfg.tokens}, hidden {main_cfg.hidden}, "
                                f"n_ff {main_cfg.n_ff}, {main_cfg.n_expert} experts, top-{main_cfg.topk} "
-                               f"{main_cfg.routing}, gate/up Q2_0, down "
+                               f"{main_cfg.routing}, gate/up {'Q2_0' if main_cfg.gu_type == 1 else 'NL4'}, down "
                                f"{'Q2_0' if main_cfg.down_type == 1 else 'NL4'}",
                    "tokens": main_cfg.tokens, "rows": main_cfg.rows, "chunk_rows": args.chunk_rows},
         "per_kernel_ms": m["per_kernel_ms"],

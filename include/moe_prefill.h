@@ -9,7 +9,7 @@
  *   moe_weights_pack   (once per layer, at load) weights -> the kernels' tiled layout
  *   moe_prefill_plan   routing ids -> expert-sorted rows, offsets, chunk table
  *   quantize_scatter   X (fp32) -> q8_1 rows, one copy per (token, expert)
- *   expert_gate_up     q8_1 rows x Q2_0 gate/up weights -> GU (fp32)
+ *   expert_gate_up     q8_1 rows x Q2_0 (or NL4) gate/up weights -> GU (fp32)
  *   swiglu_q8          GU -> q8_1 of silu(gate) * up, H never stored as floats
  *   expert_gate_up_swiglu_q8   the two above in one launch, GU never stored
  *   expert_down        q8_1 H rows x down weights -> one fp32 row per (token, expert)
@@ -83,7 +83,7 @@ typedef enum { MOE_W_Q2_0 = 1, MOE_W_NL4 = 2, MOE_W_TILED = 0x100 } moe_wtype;
  * read in place: expert e's matrix starts at base + offset[e] ("Strata"
  * PR #3752, commit list: a per-layer offset table from the expert cache's
  * base, uploaded with the group bounds).
- *   type      MOE_W_Q2_0, or MOE_W_NL4 (down product only); the plan takes
+ *   type      MOE_W_Q2_0 or MOE_W_NL4 (each product its own); the plan takes
  *             weights in the tiled layout, type | MOE_W_TILED
  *   rows      output features (gate/up: 2*n_ff; down: hidden), % 64 == 0
  *   cols      contraction length (gate/up: hidden; down: n_ff), % 64 (Q2_0)
@@ -143,7 +143,7 @@ size_t moe_plan_device_bytes(int tokens, int topk, int n_expert, int chunk_rows)
  *              twice; that gives two rows.
  *   chunk_rows 1..128: rows per chunk (the pages take 64-row chunks; one
  *              workgroup processes one chunk against 256 weight rows).
- *   w_gu       gate/up weights: Q2_0, rows = 2*n_ff, cols = hidden.
+ *   w_gu       gate/up weights: Q2_0 or NL4, rows = 2*n_ff, cols = hidden.
  *   w_down     down weights: Q2_0 or NL4, rows = hidden, cols = n_ff.
  *              Both in the tiled layout (type | MOE_W_TILED), else MOE_EFORMAT.
  *   plan_dev   device workspace of moe_plan_device_bytes(...) bytes, 16-byte

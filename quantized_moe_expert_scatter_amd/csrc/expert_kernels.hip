@@ -605,6 +605,8 @@ hipError_t launch_expert_product(const ProductArgs &a, hipStream_t stream) {
     } else {
         if (a.dots)
             hipLaunchKernelGGL((expert_product_kernel<2, kDots>), grid, block, 0, stream, a);
+        else if (a.hq)
+            hipLaunchKernelGGL((expert_product_kernel<2, kSwiglu>), grid, block, 0, stream, a);
         else
             hipLaunchKernelGGL((expert_product_kernel<2, kOut>), grid, block, 0, stream, a);
     }

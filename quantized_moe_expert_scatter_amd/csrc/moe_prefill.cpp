@@ -23,7 +23,7 @@ struct moe_plan {
     int hidden = 0, n_ff = 0;
     moe_weights gu{}, dn{};
     std::vector<uint64_t> gu_off, dn_off;
-    int8_t dn_codebook[16] = {};
+    int8_t gu_codebook[16] = {}, dn_codebook[16] = {};
     std::vector<int32_t> counts, offsets, perm, inv, chunks, dev_chunks;
     int32_t xcd_tab[2 * kXcds] = {};
     int n_chunks = 0;
@@ -54,10 +54,10 @@ size_t weight_bytes(int type, int rows, int cols) {
 
 // Shape, alignment and extent of a weight descriptor.  `tiled`: the layout
 // flag the caller must (1) or must not (0) have set.
-int check_weights(const moe_weights *w, int n_expert, bool allow_nl4, bool tiled) {
+int check_weights(const moe_weights *w, int n_expert, bool tiled) {
     if (!w || !w->base || !w->offset) return MOE_EINVAL;
     const int t = base_type(w->type);
-    if (t != MOE_W_Q2_0 && !(allow_nl4 && t == MOE_W_NL4)) return MOE_EFORMAT;
+    if (t != MOE_W_Q2_0 && t != MOE_W_NL4) return MOE_EFORMAT;
     if (((w->type & MOE_W_TILED) != 0) != tiled) return MOE_EFORMAT;
     if (w->n_expert != n_expert || w->rows <= 0 || w->cols <= 0) return MOE_EINVAL;
     if (w->rows % 64 || w->cols % block_values(t)) return MOE_EFORMAT;
@@ -86,7 +86,7 @@ size_t moe_weight_bytes(int type, int rows, int cols) { return weight_bytes(type
 
 int moe_weights_pack(const moe_weights *w, void *dst, size_t dst_bytes, void *stream) {
     if (!w || !dst) return MOE_EINVAL;
-    const int st = check_weights(w, w->n_expert, true, false);
+    const int st = check_weights(w, w->n_expert, false);
     if (st) return st;
     if (w->n_expert <= 0) return MOE_EINVAL;
     if (!aligned16(dst)) return MOE_EALIGN;
@@ -149,9 +149,9 @@ int moe_prefill_plan(const int32_t *ids, int tokens, int topk, int n_expert, int
     if (tokens > 0 && !ids) return MOE_EINVAL;
     const long long R64 = (long long)tokens * topk;
     if (R64 > (1LL << 30)) return MOE_EINVAL;
-    int st = check_weights(w_gu, n_expert, false, true);
+    int st = check_weights(w_gu, n_expert, true);
     if (st) return st;
-    st = check_weights(w_down, n_expert, true, true);
+    st = check_weights(w_down, n_expert, true);
     if (st) return st;
     if (w_gu->rows % 2 || w_down->rows != w_gu->cols || w_down->cols * 2 != w_gu->rows)
         return MOE_EINVAL;
@@ -171,9 +171,11 @@ int moe_prefill_plan(const int32_t *ids, int tokens, int topk, int n_expert, int
     p->gu = *w_gu; p->dn = *w_down;
     p->gu_off.assign(w_gu->offset, w_gu->offset + n_expert);
     p->dn_off.assign(w_down->offset, w_down->offset + n_expert);
+    if (base_type(w_gu->type) == MOE_W_NL4) std::memcpy(p->gu_codebook, w_gu->codebook, 16);
     if (base_type(w_down->type) == MOE_W_NL4) std::memcpy(p->dn_codebook, w_down->codebook, 16);
     p->gu.offset = p->gu_off.data();
     p->dn.offset = p->dn_off.data();
+    p->gu.codebook = p->gu_codebook;
     p->dn.codebook = p->dn_codebook;
     p->layout = L;
 
@@ -322,7 +324,7 @@ static ProductArgs product_args(const moe_plan *p, int product, const void *act)
     a.out_rows = w.rows;
     a.n_tiles = (w.rows + kTileRows - 1) / kTileRows;
     a.max_items = p->max_xcd_chunks * a.n_tiles;
-    if (a.wtype == MOE_W_NL4) std::memcpy(a.codebook, p->dn_codebook, 16);
+    if (a.wtype == MOE_W_NL4) std::memcpy(a.codebook, product == 0 ? p->gu_codebook : p->dn_codebook, 16);
     return a;
 }
 

@@ -66,6 +66,7 @@ class LayerConfig:
     routing: str  # "uniform" | "lognormal" | "flat32"
     down_type: int = Q2_0
     sigma: float = 1.0
+    gu_type: int = Q2_0
     x_seed: int = 0
     ids_seed: int = 0
     gu_seed: int = 0
@@ -92,6 +93,9 @@ CONFIGS = {
                        x_seed=41, ids_seed=42, gu_seed=_LAYER_GU_SEED, down_seed=_LAYER_DOWN_SEED),
     "t128": LayerConfig("t128", 128, 2560, 640, 512, 10, "uniform", down_type=NL4,
                         x_seed=51, ids_seed=52, gu_seed=_LAYER_GU_SEED, down_seed=1052),
+    # both products in NL4 (32-value blocks, codebook weights) at the 2K shape
+    "2k_nl4": LayerConfig("2k_nl4", 2048, 2560, 640, 512, 10, "uniform", down_type=NL4,
+                          gu_type=NL4, x_seed=61, ids_seed=62, gu_seed=1061, down_seed=1052),
 }
 
 
@@ -256,7 +260,7 @@ class Layer:
 def make_layer(cfg: LayerConfig, shuffle_slots: bool = False) -> Layer:
     x = activations(cfg.tokens, cfg.hidden, cfg.x_seed)
     ids = routing(cfg)
-    w_gu = expert_weights(Q2_0, 2 * cfg.n_ff, cfg.hidden, cfg.n_expert, cfg.gu_seed,
+    w_gu = expert_weights(cfg.gu_type, 2 * cfg.n_ff, cfg.hidden, cfg.n_expert, cfg.gu_seed,
                           shuffle_slots=shuffle_slots)
     w_down = expert_weights(cfg.down_type, cfg.hidden, cfg.n_ff, cfg.n_expert, cfg.down_seed,
                             shuffle_slots=shuffle_slots)
@@ -264,8 +268,9 @@ def make_layer(cfg: LayerConfig, shuffle_slots: bool = False) -> Layer:
 
 
 def small_config(name: str, tokens: int, hidden: int, n_ff: int, n_expert: int, topk: int,
-                 routing_kind: str = "uniform", down_type: int = Q2_0, seed: int = 0) -> LayerConfig:
+                 routing_kind: str = "uniform", down_type: int = Q2_0, seed: int = 0,
+                 gu_type: int = Q2_0) -> LayerConfig:
     """An ad-hoc config for tests (ragged shapes, other routings)."""
     return LayerConfig(name, tokens, hidden, n_ff, n_expert, topk, routing_kind,
-                       down_type=down_type, x_seed=seed * 10 + 1, ids_seed=seed * 10 + 2,
+                       down_type=down_type, gu_type=gu_type, x_seed=seed * 10 + 1, ids_seed=seed * 10 + 2,
                        gu_seed=seed * 10 + 3, down_seed=seed * 10 + 4)

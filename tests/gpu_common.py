@@ -22,7 +22,7 @@ def oracle_rows(L: wl.Layer, pl: oracle.Plan, rows: np.ndarray, n_threads: int =
     cfg = L.cfg
     row_e = pl.row_expert()[rows]
     xq = oracle.quantize_scatter(L.x, cfg.topk, pl.perm, rows=rows)
-    gu = oracle.expert_product(*w_tuple(L.w_gu)[:3], cfg.n_expert, 2 * cfg.n_ff, cfg.hidden, None,
+    gu = oracle.expert_product(*w_tuple(L.w_gu)[:3], cfg.n_expert, 2 * cfg.n_ff, cfg.hidden, L.w_gu.codebook,
                                xq, row_e, n_threads=n_threads)
     hq = oracle.swiglu_q8(gu, cfg.n_ff)
     dm = oracle.expert_product(L.w_down.wtype, L.w_down.buf, L.w_down.offsets, cfg.n_expert,

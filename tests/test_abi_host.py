@@ -137,8 +137,13 @@ def test_validation_errors():
         ws[which].struct.type &= ~_lib.MOE_W_TILED
         assert _plan_status(ids, 4, 64, *ws) == -3
     w_gu, w_dn = _weights(cfg)
-    w_gu.struct.type = 2                       # NL4 gate/up is not supported
-    assert _plan_status(ids, 4, 64, w_gu, w_dn) == -3
+    w_gu.struct.type = 2 | _lib.MOE_W_TILED    # NL4 gate/up needs its codebook
+    assert _plan_status(ids, 4, 64, w_gu, w_dn) == -1
+    w_gu.codebook = wl.nl4_codebook(5)
+    w_gu.struct.codebook = w_gu.codebook.ctypes.data
+    assert _plan_status(ids, 4, 64, w_gu, w_dn) == -4   # NL4 matrices are twice as large
+    w_gu.struct.base_bytes *= 2
+    assert _plan_status(ids, 4, 64, w_gu, w_dn) == 0
     w_gu, w_dn = _weights(cfg)
     w_gu.struct.cols = 96                      # not a multiple of 64 for Q2_0
     w_dn.struct.rows = 96

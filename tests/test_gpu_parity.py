@@ -34,6 +34,11 @@ SMALL = {
     "lognormal": wl.small_config("lognormal", 400, 256, 128, 32, 6, routing_kind="lognormal", seed=23),
     "one_token": wl.small_config("one_token", 1, 256, 128, 8, 2, seed=24),
     "top1": wl.small_config("top1", 130, 256, 128, 2, 1, seed=25),
+    # NL4 gate/up (Q2_0 down), and both products NL4 with about 200 rows per
+    # expert so 128-row chunks run 4-, 3-, 2- and 1-tile items
+    "nl4_gu": wl.small_config("nl4_gu", 150, 448, 192, 6, 4, gu_type=wl.NL4, seed=26),
+    "nl4_both": wl.small_config("nl4_both", 400, 512, 224, 6, 3, gu_type=wl.NL4,
+                                down_type=wl.NL4, seed=27),
 }
 
 
@@ -53,10 +58,20 @@ def _oracle_full(L):
 
 @pytest.mark.parametrize("name", list(SMALL))
 def test_small_chain_every_element(name):
+    _chain_every_element(name, 64)
+
+
+@pytest.mark.parametrize("name", ["nl4_both", "lognormal", "ragged", "nl4_gu"])
+def test_small_chain_128_row_chunks(name):
+    """The benchmark's chunk size: items of up to four 32-row tiles."""
+    _chain_every_element(name, 128)
+
+
+def _chain_every_element(name, chunk_rows):
     L = _small_layer(name)
-    _say("case", name, L.cfg)
+    _say("case", name, "chunk_rows", chunk_rows, L.cfg)
     ref = _oracle_full(L)
-    D = device_layer(L)
+    D = device_layer(L, chunk_rows=chunk_rows)
     D.run()
     torch.cuda.synchronize()
     assert np.array_equal(D.xq_host(), ref.xq), "q8_1 bytes of X"
@@ -72,7 +87,7 @@ def test_small_chain_every_element(name):
     D.close()
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged", "ragged_nl4"])
+@pytest.mark.parametrize("name", ["tiny", "ragged", "ragged_nl4", "nl4_gu"])
 def test_block_dots_bit_exact(name):
     L = _small_layer(name)
     cfg = L.cfg
@@ -95,7 +110,7 @@ def test_block_dots_bit_exact(name):
     D.close()
 
 
-@pytest.mark.parametrize("name", ["ragged", "ragged_nl4", "tiny"])
+@pytest.mark.parametrize("name", ["ragged", "ragged_nl4", "tiny", "nl4_both"])
 def test_swiglu_q8_and_down_alone_on_oracle_inputs(name):
     """swiglu_q8 fed the oracle's GU, and the down product fed the oracle's H
     (isolating it from H flips)."""
@@ -207,7 +222,7 @@ def test_fused_gate_up_swiglu_matches_two_steps(name):
 
 
 # ------------------------------------------------------------- full layers
-FULL = ["2k", "8k", "16k", "t128"]
+FULL = ["2k", "8k", "16k", "t128", "2k_nl4"]
 
 
 @pytest.mark.parametrize("name", FULL)
