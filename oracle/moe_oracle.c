@@ -294,3 +294,20 @@ void orc_swiglu_q8(const float *gu, int rows, int F, int interleaved, uint8_t *h
     }
     free(h);
 }
+
+/* --------------------------------------------------------------- combine --
+ * The step after the down product ("Strata" PR #3752 names the MoE combine
+ * among the prompt-path fusions its port leaves out; no formula is printed).
+ * Our reading is the usual weighted sum of a token's expert outputs,
+ * out[t][n] = sum over k of w[t][k] * dm[t*K + k][n], evaluated in fp32 as
+ * one fused multiply-add per term, k ascending, from 0. */
+void orc_combine(const float *dm, const float *w, int T, int K, int H, float *out)
+{
+    for (int t = 0; t < T; ++t)
+        for (int n = 0; n < H; ++n) {
+            float acc = 0.0f;
+            for (int k = 0; k < K; ++k)
+                acc = fmaf(w[(size_t)t * K + k], dm[((size_t)t * K + k) * H + n], acc);
+            out[(size_t)t * H + n] = acc;
+        }
+}

@@ -98,6 +98,11 @@ void orc_swiglu_q8(const float *gu, int rows, int F, int interleaved, uint8_t *h
 /* Unfused swiglu: h[rows][F] floats (for the composition check). */
 void orc_swiglu_rows(const float *gu, int rows, int F, int interleaved, float *h);
 
+/* MoE combine: out[T*H], out[t][n] = fmaf chain over k ascending of
+ * w[t*K+k] * dm[(t*K+k)*H + n], starting from 0.0f.  dm[T*K*H] holds one
+ * row per (token, slot), w[T*K] the routing weights. */
+void orc_combine(const float *dm, const float *w, int T, int K, int H, float *out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -59,6 +59,7 @@ def lib():
         L.orc_swiglu.restype = ctypes.c_float
         L.orc_swiglu_q8.argtypes = [P, I, I, I, P]
         L.orc_swiglu_rows.argtypes = [P, I, I, I, P]
+        L.orc_combine.argtypes = [P, P, I, I, I, P]
         _lib = L
     return _lib
 
@@ -245,6 +246,21 @@ class LayerResult:
     gu: np.ndarray   # float32 [R, 2*n_ff], expert-sorted
     hq: np.ndarray   # uint8 [R, q8_1 row of n_ff], expert-sorted
     dm: np.ndarray   # float32 [T*K, hidden], row t*K+k
+
+
+def combine(dm: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """MoE combine (the step after the down product; "Strata" PR #3752 lists
+    it among the fusions its port leaves out, without a formula): out[t] =
+    sum over k of w[t, k] * dm[t*K + k], one fp32 fmaf per term, k ascending.
+    dm: float32 [T*K, H] in (token, slot) order; w: float32 [T, K]."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    T, K = w.shape
+    dm = np.ascontiguousarray(dm, dtype=np.float32).reshape(T * K, -1)
+    H = dm.shape[1]
+    out = np.zeros((T, H), np.float32)
+    if T and H:
+        lib().orc_combine(_p(dm), _p(w), T, K, H, _p(out))
+    return out
 
 
 def layer(x, ids, n_expert, n_ff, w_gu, w_down, chunk_rows: int = 64, n_threads: int = 1) -> LayerResult:
