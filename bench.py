@@ -64,6 +64,7 @@ def algorithmic(cfg, counts):
         "swiglu_q8": R * 2 * F * 4 + R * q8(F),
         "expert_gate_up_swiglu_q8": R * q8(H) + w_gu + R * q8(F),
         "expert_down": R * q8(F) + w_dn + R * H * 4,
+        "moe_combine": R * H * 4 + R * 4 + T * H * 4,
     }
     ops = {"expert_gate_up": 2 * R * 2 * F * H, "expert_gate_up_swiglu_q8": 2 * R * 2 * F * H,
            "expert_down": 2 * R * H * F}
@@ -77,13 +78,16 @@ def algorithmic(cfg, counts):
     return by, ops, alu
 
 
-def time_layer(D, steps, warmup, fused=True):
+def time_layer(D, steps, warmup, fused=True, combine=False):
     import torch
     stream = torch.cuda.current_stream()
     if fused:
-        names, fns = KERNELS, [D.quantize_scatter, D.expert_gate_up_swiglu_q8, D.expert_down]
+        names, fns = list(KERNELS), [D.quantize_scatter, D.expert_gate_up_swiglu_q8, D.expert_down]
     else:
-        names, fns = KERNELS_4, [D.quantize_scatter, D.expert_gate_up, D.swiglu_q8, D.expert_down]
+        names, fns = list(KERNELS_4), [D.quantize_scatter, D.expert_gate_up, D.swiglu_q8, D.expert_down]
+    if combine:
+        names.append("moe_combine")
+        fns.append(D.combine)
     for _ in range(warmup):
         for f in fns:
             f()
@@ -155,7 +159,8 @@ def run_sweep(args, wl, DeviceLayer, torch):
     for name, cfg in wl.SWEEP.items():
         print(f"[sweep] {name}: generating inputs", file=sys.stderr, flush=True)
         L = wl.make_layer(cfg)
-        D = DeviceLayer(L.x, L.ids, L.w_gu, L.w_down, chunk_rows=args.chunk_rows)
+        D = DeviceLayer(L.x, L.ids, L.w_gu, L.w_down, chunk_rows=args.chunk_rows,
+                        route_w=L.route_w)
         torch.cuda.synchronize()
         counts, _, _, chunks = D.plan.query()
         n_chunks = chunks.shape[0]
@@ -220,13 +225,15 @@ def main():
         print(f"[bench] {name}: generating inputs", file=sys.stderr, flush=True)
         L = wl.make_layer(cfg)
         t0 = time.perf_counter()
-        D = DeviceLayer(L.x, L.ids, L.w_gu, L.w_down, chunk_rows=args.chunk_rows)
+        D = DeviceLayer(L.x, L.ids, L.w_gu, L.w_down, chunk_rows=args.chunk_rows,
+                        route_w=L.route_w)
         torch.cuda.synchronize()
         setup_s = time.perf_counter() - t0
         counts = D.plan.query()[0]
         steps = args.steps if name == args.workload else max(5, args.steps // 5)
         ms, per_kernel = time_layer(D, steps, args.warmup)
         ms4, per_kernel4 = time_layer(D, max(3, steps // 5), 1, fused=False)
+        msc, per_kernelc = time_layer(D, max(3, steps // 5), 1, combine=True)
         by, ops, alu = algorithmic(cfg, counts)
         useful_ops = ops["expert_gate_up"] + ops["expert_down"]
         step_bytes = sum(by[k] for k in KERNELS)
@@ -236,6 +243,10 @@ def main():
                          "hbm_floor_ms": round(step_bytes / (HBM_PEAK_GBS * 1e9) * 1e3, 4),
                          "four_launch": {"ms_per_layer": round(ms4, 4),
                                          "per_kernel_ms": {k: round(v, 4) for k, v in per_kernel4.items()}},
+                         "with_combine": {"ms_per_layer": round(msc, 4),
+                                          "combine_ms": round(per_kernelc["moe_combine"], 4),
+                                          "combine_gbs": round(by["moe_combine"] /
+                                                               (per_kernelc["moe_combine"] * 1e-3) / 1e9, 1)},
                          "steps": steps, "setup_s": round(setup_s, 2)}
         print(f"[bench] {name}: {ms:.3f} ms/layer {results[name]['tops']} TOPS {per_kernel}",
               file=sys.stderr, flush=True)
@@ -289,7 +300,7 @@ def main():
         "per_kernel_ms": m["per_kernel_ms"],
         "hbm_floor_ms": m["hbm_floor_ms"],
         "layers": {k: {kk: v[kk] for kk in ("ms_per_layer", "tops", "per_kernel_ms", "hbm_floor_ms",
-                                            "four_launch")}
+                                            "four_launch", "with_combine")}
                    for k, v in results.items()},
         "roofline": roof,
         "cpu_baseline": cpu,

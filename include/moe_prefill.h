@@ -13,6 +13,7 @@
  *   swiglu_q8          GU -> q8_1 of silu(gate) * up, H never stored as floats
  *   expert_gate_up_swiglu_q8   the two above in one launch, GU never stored
  *   expert_down        q8_1 H rows x down weights -> one fp32 row per (token, expert)
+ *   moe_combine        routing-weighted sum of each token's expert rows -> [tokens x hidden]
  *
  * Conventions shared by every entry point:
  *   - Device pointers are HIP device addresses on the current device; host
@@ -208,6 +209,17 @@ int expert_gate_up_swiglu_q8(const moe_plan *plan, const void *xq, void *hq, voi
  * hq: device q8_1 rows [tokens*topk x n_ff]; dm: device fp32
  * [tokens*topk x hidden], 16-byte aligned. */
 int expert_down(const moe_plan *plan, const void *hq, float *dm, void *stream);
+
+/* The MoE combine, the step after step 4 (the pages name it among the
+ * prompt-path fusions PR #3752 leaves out and print no formula; this is the
+ * plain routing-weighted sum):
+ *   out[t][n] = sum over k of w[t*topk+k] * dm[t*topk+k][n],
+ * evaluated in fp32 as one fmaf per term, k ascending, starting from 0.
+ * dm: device fp32 [tokens*topk x hidden] as expert_down writes it; w: device
+ * fp32 [tokens x topk] routing weights; out: device fp32 [tokens x hidden];
+ * all 16-byte aligned.  MOE_EINVAL if tokens * ceil(hidden/1024) * 256
+ * exceeds 2^32 - 1 (the launch's thread count). */
+int moe_combine(const moe_plan *plan, const float *dm, const float *w, float *out, void *stream);
 
 /* Test export: the exact int32 dots of every (sorted row, output, 32-value
  * block) of one product, computed by the same kernel path as the product.

@@ -26,7 +26,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EALIGN", -3: "MOE_EFORMAT",
 EXPORTS = ["moe_q8_1_bytes", "moe_weight_bytes", "moe_weights_pack", "moe_plan_device_bytes",
            "moe_prefill_plan",
            "moe_plan_query", "moe_plan_destroy", "quantize_scatter", "expert_gate_up",
-           "swiglu_q8", "expert_gate_up_swiglu_q8", "expert_down", "moe_debug_block_dots",
+           "swiglu_q8", "expert_gate_up_swiglu_q8", "expert_down", "moe_combine",
+           "moe_debug_block_dots",
            "moe_status_string"]
 
 
@@ -75,6 +76,8 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.argtypes = [P, P, P, P]
             f.restype = I
+        L.moe_combine.argtypes = [P, P, P, P, P]
+        L.moe_combine.restype = I
         L.moe_debug_block_dots.argtypes = [P, I, P, I, I, P, P]
         L.moe_debug_block_dots.restype = I
         L.moe_status_string.argtypes = [I]
@@ -221,6 +224,10 @@ def expert_gate_up_swiglu_q8(plan: Plan, xq, hq, stream=None):
 
 def expert_down(plan: Plan, hq, dm, stream=None):
     _check(lib().expert_down(plan.handle, _ptr(hq), _ptr(dm), _stream(stream)), "expert_down")
+
+
+def moe_combine(plan: Plan, dm, w, out, stream=None):
+    _check(lib().moe_combine(plan.handle, _ptr(dm), _ptr(w), _ptr(out), _stream(stream)), "moe_combine")
 
 
 def moe_debug_block_dots(plan: Plan, product: int, act, row_begin: int, n_rows: int, dots,

@@ -1,0 +1,64 @@
+// combine_kernels.hip -- the MoE combine after the down product: each token's
+// output row is the routing-weighted sum of its topk expert rows.
+//
+// "Strata" PR #3752 names the combine among the prompt-path fusions its port
+// leaves out and prints no formula; the reading here is the plain weighted
+// sum, one fp32 fused multiply-add per term in slot order from zero:
+//   out[t][n] = fmaf(w[t][K-1], dm[t*K+K-1][n], ... fmaf(w[t][0], dm[t*K][n], 0))
+// The down product writes dm in (token, slot) order, so a token's K rows are
+// consecutive and every read and write is a contiguous float4 run: the kernel
+// is bound by HBM (K + 1 rows of H floats per token).
+#include "internal.h"
+
+#include <hip/hip_runtime.h>
+
+namespace moe {
+
+namespace {
+
+constexpr int kCombineThreads = 256;   // one float4 of one token per thread
+constexpr int kCombineBatch = 8;       // slots whose loads are issued together
+
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float *dm, const float *w,
+                                                                  float *out, int topk, int h4,
+                                                                  int blocks_per_token) {
+    const int t = blockIdx.x / blocks_per_token;
+    const int c = (blockIdx.x - t * blocks_per_token) * kCombineThreads + threadIdx.x;
+    if (c >= h4) return;
+    const float4 *src = reinterpret_cast<const float4 *>(dm) + size_t(t) * topk * h4 + c;
+    const float *wt = w + size_t(t) * topk;
+    float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k0 = 0; k0 < topk; k0 += kCombineBatch) {
+        float4 d[kCombineBatch];
+        float wk[kCombineBatch];
+#pragma unroll
+        for (int j = 0; j < kCombineBatch; ++j)
+            if (k0 + j < topk) {
+                d[j] = src[size_t(k0 + j) * h4];
+                wk[j] = wt[k0 + j];
+            }
+#pragma unroll
+        for (int j = 0; j < kCombineBatch; ++j)
+            if (k0 + j < topk) {
+                acc.x = __builtin_fmaf(wk[j], d[j].x, acc.x);
+                acc.y = __builtin_fmaf(wk[j], d[j].y, acc.y);
+                acc.z = __builtin_fmaf(wk[j], d[j].z, acc.z);
+                acc.w = __builtin_fmaf(wk[j], d[j].w, acc.w);
+            }
+    }
+    reinterpret_cast<float4 *>(out)[size_t(t) * h4 + c] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float *dm, const float *w, int tokens, int topk, int hidden,
+                          float *out, hipStream_t stream) {
+    if (tokens <= 0 || hidden <= 0) return hipSuccess;
+    const int h4 = hidden / 4;
+    const int per_token = (h4 + kCombineThreads - 1) / kCombineThreads;
+    const dim3 grid(unsigned(tokens) * unsigned(per_token)), block(kCombineThreads);
+    hipLaunchKernelGGL(combine_kernel, grid, block, 0, stream, dm, w, out, topk, h4, per_token);
+    return hipGetLastError();
+}
+
+}  // namespace moe

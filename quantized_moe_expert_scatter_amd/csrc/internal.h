@@ -73,6 +73,10 @@ hipError_t launch_quantize_scatter(const float *x, int tokens, int hidden, int t
 hipError_t launch_swiglu_q8(const float *gu, int rows, int n_ff, uint8_t *hq,
                             hipStream_t stream);
 hipError_t launch_expert_product(const ProductArgs &args, hipStream_t stream);
+// out[t] = sum over k of w[t*topk+k] * dm[t*topk+k] (fmaf, k ascending);
+// the grid is tokens * ceil(hidden / 1024) workgroups of 256 threads.
+hipError_t launch_combine(const float *dm, const float *w, int tokens, int topk, int hidden,
+                          float *out, hipStream_t stream);
 // Packs n_expert matrices of rows x blocks_per_row blocks into the tiled
 // layout; expert e's planes start at src/dst + e * expert_stride.
 hipError_t launch_weight_pack(const uint8_t *src, uint8_t *dst, uint64_t expert_stride,

@@ -374,6 +374,19 @@ int expert_down(const moe_plan *p, const void *hq, float *dm, void *stream) {
     return hip_status(launch_expert_product(a, static_cast<hipStream_t>(stream)));
 }
 
+int moe_combine(const moe_plan *p, const float *dm, const float *w, float *out, void *stream) {
+    int st = ready(p);
+    if (st) return st;
+    if (p->rows == 0) return MOE_OK;
+    if (!dm || !w || !out) return MOE_EINVAL;
+    if (!aligned16(dm) || !aligned16(w) || !aligned16(out)) return MOE_EALIGN;
+    // one workgroup of 256 threads per 1024 outputs of a token
+    const uint64_t threads = uint64_t(p->tokens) * uint64_t((p->hidden + 1023) / 1024) * 256u;
+    if (threads > 0xFFFFFFFFull) return MOE_EINVAL;
+    return hip_status(launch_combine(dm, w, p->tokens, p->topk, p->hidden, out,
+                                     static_cast<hipStream_t>(stream)));
+}
+
 int moe_debug_block_dots(const moe_plan *p, int product, const void *act, int row_begin,
                          int n_rows, int32_t *dots, void *stream) {
     int st = ready(p);

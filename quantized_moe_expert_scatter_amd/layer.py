@@ -26,7 +26,7 @@ class DeviceLayer:
     """
 
     def __init__(self, x: np.ndarray, ids: np.ndarray, w_gu: ExpertWeights, w_down: ExpertWeights,
-                 chunk_rows: int = 128, device="cuda", stream=None):
+                 chunk_rows: int = 128, device="cuda", stream=None, route_w: np.ndarray = None):
         import torch
         self.device = torch.device(device)
         self.tokens, self.hidden = x.shape
@@ -51,6 +51,12 @@ class DeviceLayer:
                               device=self.device)
         self.dm = torch.empty((max(self.rows, 1), self.hidden), dtype=torch.float32,
                               device=self.device)
+        # the combine's routing weights [T, topk] and output [T, hidden]
+        rw = np.zeros((self.tokens, self.topk), np.float32) if route_w is None else route_w
+        self.route_w = _to_device(rw.astype(np.float32, copy=False).reshape(-1)
+                                  if rw.size else np.zeros(4, np.float32), self.device)
+        self.out = torch.empty((max(self.tokens, 1), self.hidden), dtype=torch.float32,
+                               device=self.device)
         self.plan = _lib.moe_prefill_plan(ids, self.n_expert, chunk_rows, self.w_gu, self.w_dn,
                                           workspace=self.workspace, stream=stream)
 
@@ -80,6 +86,9 @@ class DeviceLayer:
     def expert_down(self, stream=None):
         _lib.expert_down(self.plan, self.hq, self.dm, stream)
 
+    def combine(self, stream=None):
+        _lib.moe_combine(self.plan, self.dm, self.route_w, self.out, stream)
+
     def run(self, stream=None):
         """The four steps, one launch each (GU materialised)."""
         self.quantize_scatter(stream)
@@ -108,6 +117,9 @@ class DeviceLayer:
 
     def dm_host(self) -> np.ndarray:
         return self.dm[: self.rows].cpu().numpy()
+
+    def out_host(self) -> np.ndarray:
+        return self.out[: self.tokens].cpu().numpy()
 
     def close(self):
         self.plan.close()

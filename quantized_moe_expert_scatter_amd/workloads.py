@@ -169,6 +169,16 @@ def routing_flat(tokens: int, n_expert: int, topk: int, per_expert: int, seed: i
     return experts[flat].reshape(tokens, topk)
 
 
+def routing_weights(tokens: int, topk: int, seed: int) -> np.ndarray:
+    """float32 [T, topk]: a softmax over the token's topk of standard normal
+    logits (what a router hands the combine), computed in float64."""
+    z = np.random.default_rng(seed).standard_normal((tokens, topk))
+    if tokens == 0:
+        return z.astype(np.float32)
+    e = np.exp(z - z.max(axis=1, keepdims=True))
+    return (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
 def routing(cfg: LayerConfig) -> np.ndarray:
     if cfg.routing == "uniform":
         return routing_uniform(cfg.tokens, cfg.n_expert, cfg.topk, cfg.ids_seed)
@@ -254,6 +264,7 @@ class Layer:
     ids: np.ndarray
     w_gu: ExpertWeights
     w_down: ExpertWeights
+    route_w: Optional[np.ndarray] = None     # float32 [T, topk] routing weights
     extra: dict = field(default_factory=dict)
 
 
@@ -264,7 +275,8 @@ def make_layer(cfg: LayerConfig, shuffle_slots: bool = False) -> Layer:
                           shuffle_slots=shuffle_slots)
     w_down = expert_weights(cfg.down_type, cfg.hidden, cfg.n_ff, cfg.n_expert, cfg.down_seed,
                             shuffle_slots=shuffle_slots)
-    return Layer(cfg, x, ids, w_gu, w_down)
+    route_w = routing_weights(cfg.tokens, cfg.topk, cfg.ids_seed + 5003)
+    return Layer(cfg, x, ids, w_gu, w_down, route_w)
 
 
 def small_config(name: str, tokens: int, hidden: int, n_ff: int, n_expert: int, topk: int,

@@ -10,7 +10,7 @@ from quantized_moe_expert_scatter_amd.layer import DeviceLayer
 
 
 def device_layer(L: wl.Layer, chunk_rows: int = 64) -> DeviceLayer:
-    return DeviceLayer(L.x, L.ids, L.w_gu, L.w_down, chunk_rows=chunk_rows)
+    return DeviceLayer(L.x, L.ids, L.w_gu, L.w_down, chunk_rows=chunk_rows, route_w=L.route_w)
 
 
 def w_tuple(w: wl.ExpertWeights):

@@ -176,6 +176,8 @@ def test_host_only_plan_refuses_kernels():
               L.expert_down):
         assert f(plan.handle, FAKE_BASE, FAKE_BASE, None) == -6
         assert f(None, FAKE_BASE, FAKE_BASE, None) == -1
+    assert L.moe_combine(plan.handle, FAKE_BASE, FAKE_BASE, FAKE_BASE, None) == -6
+    assert L.moe_combine(None, FAKE_BASE, FAKE_BASE, FAKE_BASE, None) == -1
     assert L.moe_debug_block_dots(plan.handle, 0, FAKE_BASE, 0, 1, FAKE_BASE, None) == -6
     assert L.quantize_scatter(None, FAKE_BASE, FAKE_BASE, None) == -1
     with pytest.raises(_lib.MoeError):

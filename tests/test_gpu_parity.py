@@ -221,6 +221,26 @@ def test_fused_gate_up_swiglu_matches_two_steps(name):
     D.close()
 
 
+@pytest.mark.parametrize("name", ["tiny", "ragged", "nl4_both", "top1", "one_token"])
+def test_combine(name):
+    """moe_combine is bit-exact against the oracle's combine of the same dm,
+    and the whole chain with the combine stays within the output tolerance."""
+    L = _small_layer(name)
+    _say("case", name)
+    ref = _oracle_full(L)
+    D = device_layer(L)
+    D.run()
+    D.out.fill_(float("nan"))
+    D.combine()
+    torch.cuda.synchronize()
+    out = D.out_host()
+    exp = oracle.combine(D.dm_host(), L.route_w)
+    assert np.array_equal(out.view(np.uint32), exp.view(np.uint32))
+    e = rel_rms(out, oracle.combine(ref.dm, L.route_w))
+    assert e <= 1e-2 if flip_rows(D.hq_host(), ref.hq).size else e <= 1e-5, e
+    D.close()
+
+
 # ------------------------------------------------------------- full layers
 FULL = ["2k", "8k", "16k", "t128", "2k_nl4"]
 
@@ -272,6 +292,16 @@ def _sampled_rows(cfg):
     for t in range(4):
         rs = tok_rows[t * cfg.topk:(t + 1) * cfg.topk]
         assert all(np.array_equal(xq_dev[rs[0]], xq_dev[r]) for r in rs)
+    # the combine on sampled tokens, against the oracle's combine of the device's dm
+    D.combine()
+    torch.cuda.synchronize()
+    toks = np.unique(np.concatenate([rng.choice(cfg.tokens, min(cfg.tokens, 48), replace=False),
+                                     [0, cfg.tokens - 1]]))
+    slots = (toks[:, None] * cfg.topk + np.arange(cfg.topk)).reshape(-1)
+    dm_tok = D.dm[torch.from_numpy(slots).cuda()].cpu().numpy()
+    exp = oracle.combine(dm_tok, L.route_w[toks])
+    got = D.out[torch.from_numpy(toks).cuda()].cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), exp.view(np.uint32)), "combine"
     # the fused gate/up + swiglu launch the benchmark times: same bytes, whole layer
     _fused_equals_two_steps(D)
     _say("fused path equal")
