@@ -110,6 +110,33 @@ def time_layer(D, steps, warmup, fused=True, combine=False):
     return total_ms / steps, per_kernel
 
 
+def time_plans(D, L, chunk_rows, reps=5):
+    """The plan built on the host (sort + upload, wall clock to completion) and
+    on the device from device ids (GPU time of its launches), median of reps."""
+    import torch
+    from quantized_moe_expert_scatter_amd import _lib
+    cfg = L.cfg
+    ws = torch.empty_like(D.workspace)
+    ids_dev = torch.from_numpy(np.ascontiguousarray(L.ids, np.int32).reshape(-1).copy()).cuda()
+    host, dev = [], []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        p = _lib.moe_prefill_plan(L.ids, cfg.n_expert, chunk_rows, D.w_gu, D.w_dn, workspace=ws)
+        torch.cuda.synchronize()
+        host.append((time.perf_counter() - t0) * 1e3)
+        p.close()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        p = _lib.moe_prefill_plan_device(ids_dev, cfg.tokens, cfg.topk, cfg.n_expert, chunk_rows,
+                                         D.w_gu, D.w_dn, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        dev.append(e0.elapsed_time(e1))
+        p.close()
+    return {"host_ms": round(float(np.median(host)), 3), "device_ms": round(float(np.median(dev)), 3)}
+
+
 def traffic_for(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source (else None)."""
@@ -247,6 +274,7 @@ def main():
                                           "combine_ms": round(per_kernelc["moe_combine"], 4),
                                           "combine_gbs": round(by["moe_combine"] /
                                                                (per_kernelc["moe_combine"] * 1e-3) / 1e9, 1)},
+                         "plan": time_plans(D, L, args.chunk_rows),
                          "steps": steps, "setup_s": round(setup_s, 2)}
         print(f"[bench] {name}: {ms:.3f} ms/layer {results[name]['tops']} TOPS {per_kernel}",
               file=sys.stderr, flush=True)
@@ -300,7 +328,7 @@ def main():
         "per_kernel_ms": m["per_kernel_ms"],
         "hbm_floor_ms": m["hbm_floor_ms"],
         "layers": {k: {kk: v[kk] for kk in ("ms_per_layer", "tops", "per_kernel_ms", "hbm_floor_ms",
-                                            "four_launch", "with_combine")}
+                                            "four_launch", "with_combine", "plan")}
                    for k, v in results.items()},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -8,6 +8,7 @@
  *
  *   moe_weights_pack   (once per layer, at load) weights -> the kernels' tiled layout
  *   moe_prefill_plan   routing ids -> expert-sorted rows, offsets, chunk table
+ *   moe_prefill_plan_device   the same plan built on the GPU from device ids
  *   quantize_scatter   X (fp32) -> q8_1 rows, one copy per (token, expert)
  *   expert_gate_up     q8_1 rows x Q2_0 (or NL4) gate/up weights -> GU (fp32)
  *   swiglu_q8          GU -> q8_1 of silu(gate) * up, H never stored as floats
@@ -161,7 +162,31 @@ int moe_prefill_plan(const int32_t *ids_host, int tokens, int topk, int n_expert
                      int chunk_rows, const moe_weights *w_gu, const moe_weights *w_down,
                      void *plan_dev, size_t plan_dev_bytes, void *stream, moe_plan **out);
 
+/* The same plan built on the device from routing ids that live there (the
+ * pages build the bounds and the chunk table on the host and upload them,
+ * PR #3752 commit list; a router on the GPU leaves its ids in device memory).
+ * Arguments as moe_prefill_plan, except:
+ *   ids_dev    device int32 [tokens*topk], 16-byte aligned, read by kernels
+ *              enqueued on `stream` (it must stay valid until they ran).
+ *   plan_dev   required.  Every section the kernels read holds the same bytes
+ *              as a host-built plan of the same ids.
+ * Nothing is read back: the call enqueues a host-to-device copy of the two
+ * weight offset tables and five small integer kernels (clear; count; prefix,
+ * expert ranking and XCD dealing in one workgroup; a stable ballot compaction
+ * per expert; the chunk lists), then returns.  An id outside [0, n_expert)
+ * cannot be refused at the call: its rows join no product (their outputs are
+ * left unwritten) and moe_plan_query on the plan returns MOE_EINVAL.  Because
+ * the per-XCD chunk counts stay on the device, the product launches over such
+ * a plan size their grids for the largest possible list (tokens*topk /
+ * chunk_rows + n_expert + 1 chunks per XCD); the surplus workgroups exit at
+ * once. */
+int moe_prefill_plan_device(const int32_t *ids_dev, int tokens, int topk, int n_expert,
+                            int chunk_rows, const moe_weights *w_gu, const moe_weights *w_down,
+                            void *plan_dev, size_t plan_dev_bytes, void *stream, moe_plan **out);
+
 /* Host view of a plan, for inspection and tests: any pointer may be NULL.
+ * For a device-built plan it waits for the plan's kernels and reads the plan
+ * back (MOE_EINVAL if a routing id was out of range).
  * counts [n_expert], offsets [n_expert+1], perm [tokens*topk] (sorted row ->
  * t*topk+k), chunks [4*n_chunks] (expert, first row, rows, 0). */
 int moe_plan_query(const moe_plan *plan, int *rows, int *n_chunks,

@@ -29,7 +29,20 @@ struct PlanLayout {
     size_t xcd;      // int32 [2*kXcds]: first chunk and chunk count of each XCD list
     size_t gu_off;   // uint64 [E]    gate/up expert byte offsets
     size_t dn_off;   // uint64 [E]    down expert byte offsets
+    // built on the device only (moe_prefill_plan_device); zero in a host plan
+    size_t counts;   // int32 [E+1]   rows per expert, then ids out of range
+    size_t offsets;  // int32 [E+2]   exclusive prefix of counts
+    size_t aux;      // int32 [kPlanAux(E)]: see PlanAux
     size_t total;
+};
+
+// Scratch of the device-built plan, int32 indices into the aux section.
+struct PlanAux {
+    static constexpr int order(int e) { return e; }                        // experts by rank
+    static constexpr int xcd_of(int n_expert, int e) { return n_expert + e; }   // XCD of expert e
+    static constexpr int base_of(int n_expert, int e) { return 2 * n_expert + e; }  // first slot in its list
+    static constexpr int status(int n_expert) { return 3 * n_expert; }     // ids out of range
+    static constexpr int size(int n_expert) { return 3 * n_expert + 4; }
 };
 
 inline PlanLayout plan_layout(int tokens, int topk, int n_expert, int chunk_rows) {
@@ -42,6 +55,9 @@ inline PlanLayout plan_layout(int tokens, int topk, int n_expert, int chunk_rows
     L.xcd = o;    o += align16(size_t(2 * kXcds) * 4);
     L.gu_off = o; o += align16(size_t(n_expert) * 8);
     L.dn_off = o; o += align16(size_t(n_expert) * 8);
+    L.counts = o; o += align16(size_t(n_expert + 1) * 4);
+    L.offsets = o; o += align16(size_t(n_expert + 2) * 4);
+    L.aux = o;    o += align16(size_t(PlanAux::size(n_expert)) * 4);
     L.total = o;
     return L;
 }
@@ -73,6 +89,10 @@ hipError_t launch_quantize_scatter(const float *x, int tokens, int hidden, int t
 hipError_t launch_swiglu_q8(const float *gu, int rows, int n_ff, uint8_t *hq,
                             hipStream_t stream);
 hipError_t launch_expert_product(const ProductArgs &args, hipStream_t stream);
+// The plan built on the device from device routing ids (see plan_kernels.hip):
+// the perm, inv, chunk, xcd, counts, offsets and aux sections of `ws`.
+hipError_t launch_device_plan(const int32_t *ids, int rows, int n_expert, int chunk_rows,
+                              uint8_t *ws, const PlanLayout &L, hipStream_t stream);
 // out[t] = sum over k of w[t*topk+k] * dm[t*topk+k] (fmaf, k ascending);
 // the grid is tokens * ceil(hidden / 1024) workgroups of 256 threads.
 hipError_t launch_combine(const float *dm, const float *w, int tokens, int topk, int hidden,

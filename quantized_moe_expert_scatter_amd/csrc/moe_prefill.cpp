@@ -28,6 +28,7 @@ struct moe_plan {
     int32_t xcd_tab[2 * kXcds] = {};
     int n_chunks = 0;
     int max_xcd_chunks = 0;
+    bool device_built = false;   // sorted maps and chunk lists built on the device
     void *plan_dev = nullptr;
     PlanLayout layout{};
     void *staging = nullptr;
@@ -72,6 +73,86 @@ int check_weights(const moe_weights *w, int n_expert, bool tiled) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+}  // namespace
+
+namespace {
+
+// Argument checks shared by the host- and device-built plans.
+int check_plan_args(int tokens, int topk, int n_expert, int chunk_rows, const moe_weights *w_gu,
+                    const moe_weights *w_down) {
+    if (tokens < 0 || topk <= 0 || n_expert <= 0 || chunk_rows <= 0 || chunk_rows > kMaxChunkRows)
+        return MOE_EINVAL;
+    if ((long long)tokens * topk > (1LL << 30)) return MOE_EINVAL;
+    int st = check_weights(w_gu, n_expert, true);
+    if (st) return st;
+    st = check_weights(w_down, n_expert, true);
+    if (st) return st;
+    if (w_gu->rows % 2 || w_down->rows != w_gu->cols || w_down->cols * 2 != w_gu->rows)
+        return MOE_EINVAL;
+    return MOE_OK;
+}
+
+moe_plan *new_plan(int tokens, int topk, int n_expert, int chunk_rows, const moe_weights *w_gu,
+                   const moe_weights *w_down) {
+    moe_plan *p = new (std::nothrow) moe_plan;
+    if (!p) return nullptr;
+    p->tokens = tokens; p->topk = topk; p->n_expert = n_expert; p->chunk_rows = chunk_rows;
+    p->rows = tokens * topk; p->hidden = w_gu->cols; p->n_ff = w_gu->rows / 2;
+    p->gu = *w_gu; p->dn = *w_down;
+    p->gu_off.assign(w_gu->offset, w_gu->offset + n_expert);
+    p->dn_off.assign(w_down->offset, w_down->offset + n_expert);
+    if (base_type(w_gu->type) == MOE_W_NL4) std::memcpy(p->gu_codebook, w_gu->codebook, 16);
+    if (base_type(w_down->type) == MOE_W_NL4) std::memcpy(p->dn_codebook, w_down->codebook, 16);
+    p->gu.offset = p->gu_off.data();
+    p->dn.offset = p->dn_off.data();
+    p->gu.codebook = p->gu_codebook;
+    p->dn.codebook = p->dn_codebook;
+    p->layout = plan_layout(tokens, topk, n_expert, chunk_rows);
+    return p;
+}
+
+// Experts largest first, ties by lower id.
+std::vector<int> expert_order(const std::vector<int32_t> &counts) {
+    std::vector<int> order(counts.size());
+    for (size_t e = 0; e < counts.size(); ++e) order[e] = int(e);
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return counts[a] > counts[b]; });
+    return order;
+}
+
+// Chunks (expert, first row, rows, 0) of the experts in `order`, each in row order.
+std::vector<int32_t> chunk_list(const std::vector<int> &order, const std::vector<int32_t> &counts,
+                                const std::vector<int32_t> &offsets, int chunk_rows) {
+    std::vector<int32_t> chunks;
+    for (int e : order)
+        for (int r0 = 0; r0 < counts[e]; r0 += chunk_rows)
+            chunks.insert(chunks.end(), {e, offsets[e] + r0, std::min(chunk_rows, counts[e] - r0), 0});
+    return chunks;
+}
+
+// Pinned staging of workspace bytes [begin, end), copied up asynchronously on
+// `stream`; p->uploaded is recorded after `then` (further work on the stream).
+template <class Fill, class Then>
+int upload(moe_plan *p, size_t begin, size_t end, void *stream, Fill fill, Then then) {
+    const size_t n = end - begin;
+    if (hipHostMalloc(&p->staging, n > 0 ? n : 16, hipHostMallocDefault) != hipSuccess) {
+        p->staging = nullptr;
+        return MOE_EHIP;
+    }
+    uint8_t *s = static_cast<uint8_t *>(p->staging);
+    std::memset(s, 0, n);
+    fill(s - begin);                      // fill writes at workspace offsets
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (hipEventCreateWithFlags(&p->uploaded, hipEventDisableTiming) != hipSuccess) {
+        p->uploaded = nullptr;
+        return MOE_EHIP;
+    }
+    if (n > 0 && hipMemcpyAsync(static_cast<uint8_t *>(p->plan_dev) + begin, s, n,
+                                hipMemcpyHostToDevice, hs) != hipSuccess)
+        return MOE_EHIP;
+    if (then(hs) != hipSuccess || hipEventRecord(p->uploaded, hs) != hipSuccess) return MOE_EHIP;
+    return MOE_OK;
+}
 
 }  // namespace
 
@@ -139,23 +220,16 @@ const char *moe_status_string(int s) {
     }
 }
 
+
 int moe_prefill_plan(const int32_t *ids, int tokens, int topk, int n_expert, int chunk_rows,
                      const moe_weights *w_gu, const moe_weights *w_down, void *plan_dev,
                      size_t plan_dev_bytes, void *stream, moe_plan **out) {
     if (!out) return MOE_EINVAL;
     *out = nullptr;
-    if (tokens < 0 || topk <= 0 || n_expert <= 0 || chunk_rows <= 0 || chunk_rows > kMaxChunkRows)
-        return MOE_EINVAL;
+    int st = check_plan_args(tokens, topk, n_expert, chunk_rows, w_gu, w_down);
+    if (st) return st;
     if (tokens > 0 && !ids) return MOE_EINVAL;
-    const long long R64 = (long long)tokens * topk;
-    if (R64 > (1LL << 30)) return MOE_EINVAL;
-    int st = check_weights(w_gu, n_expert, true);
-    if (st) return st;
-    st = check_weights(w_down, n_expert, true);
-    if (st) return st;
-    if (w_gu->rows % 2 || w_down->rows != w_gu->cols || w_down->cols * 2 != w_gu->rows)
-        return MOE_EINVAL;
-    const int R = int(R64);
+    const int R = tokens * topk;
     for (int i = 0; i < R; ++i)
         if (ids[i] < 0 || ids[i] >= n_expert) return MOE_EINVAL;
     const PlanLayout L = plan_layout(tokens, topk, n_expert, chunk_rows);
@@ -163,21 +237,8 @@ int moe_prefill_plan(const int32_t *ids, int tokens, int topk, int n_expert, int
         if (!aligned16(plan_dev)) return MOE_EALIGN;
         if (plan_dev_bytes < L.total) return MOE_ESIZE;
     }
-
-    moe_plan *p = new (std::nothrow) moe_plan;
+    moe_plan *p = new_plan(tokens, topk, n_expert, chunk_rows, w_gu, w_down);
     if (!p) return MOE_EINVAL;
-    p->tokens = tokens; p->topk = topk; p->n_expert = n_expert; p->chunk_rows = chunk_rows;
-    p->rows = R; p->hidden = w_gu->cols; p->n_ff = w_gu->rows / 2;
-    p->gu = *w_gu; p->dn = *w_down;
-    p->gu_off.assign(w_gu->offset, w_gu->offset + n_expert);
-    p->dn_off.assign(w_down->offset, w_down->offset + n_expert);
-    if (base_type(w_gu->type) == MOE_W_NL4) std::memcpy(p->gu_codebook, w_gu->codebook, 16);
-    if (base_type(w_down->type) == MOE_W_NL4) std::memcpy(p->dn_codebook, w_down->codebook, 16);
-    p->gu.offset = p->gu_off.data();
-    p->dn.offset = p->dn_off.data();
-    p->gu.codebook = p->gu_codebook;
-    p->dn.codebook = p->dn_codebook;
-    p->layout = L;
 
     // counting sort by expert, stable in t*K+k
     p->counts.assign(n_expert, 0);
@@ -194,24 +255,15 @@ int moe_prefill_plan(const int32_t *ids, int tokens, int topk, int n_expert, int
             p->inv[i] = r;
         }
     }
-
-    // experts largest first (ties: lower id first), then their chunks
-    std::vector<int> order(n_expert);
-    for (int e = 0; e < n_expert; ++e) order[e] = e;
-    std::stable_sort(order.begin(), order.end(),
-                     [&](int a, int b) { return p->counts[a] > p->counts[b]; });
-    for (int e : order)
-        for (int r0 = 0; r0 < p->counts[e]; r0 += chunk_rows) {
-            const int nr = std::min(chunk_rows, p->counts[e] - r0);
-            p->chunks.insert(p->chunks.end(), {e, p->offsets[e] + r0, nr, 0});
-        }
+    const std::vector<int> order = expert_order(p->counts);
+    p->chunks = chunk_list(order, p->counts, p->offsets, chunk_rows);
     p->n_chunks = int(p->chunks.size() / 4);
 
     // XCD work lists: every chunk of an expert goes to one XCD so that its
     // weights and activation rows are re-read from that XCD's L2; experts are
     // dealt largest first to the XCD with the fewest rows so far.
     {
-        std::vector<std::vector<int32_t>> lists(kXcds);
+        std::vector<std::vector<int>> members(kXcds);
         long long load[kXcds] = {};
         for (int e : order) {
             if (p->counts[e] == 0) continue;
@@ -219,48 +271,73 @@ int moe_prefill_plan(const int32_t *ids, int tokens, int topk, int n_expert, int
             for (int k = 1; k < kXcds; ++k)
                 if (load[k] < load[x]) x = k;
             load[x] += p->counts[e];
-            for (int r0 = 0; r0 < p->counts[e]; r0 += chunk_rows) {
-                const int nr = std::min(chunk_rows, p->counts[e] - r0);
-                lists[x].insert(lists[x].end(), {e, p->offsets[e] + r0, nr, 0});
-            }
+            members[x].push_back(e);
         }
         int start = 0;
         for (int x = 0; x < kXcds; ++x) {
-            const int cnt = int(lists[x].size() / 4);
+            const std::vector<int32_t> list = chunk_list(members[x], p->counts, p->offsets, chunk_rows);
+            const int cnt = int(list.size() / 4);
             p->xcd_tab[x] = start;
             p->xcd_tab[kXcds + x] = cnt;
             start += cnt;
             p->max_xcd_chunks = std::max(p->max_xcd_chunks, cnt);
-            p->dev_chunks.insert(p->dev_chunks.end(), lists[x].begin(), lists[x].end());
+            p->dev_chunks.insert(p->dev_chunks.end(), list.begin(), list.end());
         }
     }
 
     if (plan_dev) {
         p->plan_dev = plan_dev;
-        if (hipHostMalloc(&p->staging, L.total, hipHostMallocDefault) != hipSuccess) {
-            p->staging = nullptr;
+        st = upload(p, 0, L.total, stream,
+                    [&](uint8_t *s) {
+                        std::memcpy(s + L.perm, p->perm.data(), size_t(R) * 4);
+                        std::memcpy(s + L.inv, p->inv.data(), size_t(R) * 4);
+                        std::memcpy(s + L.chunks, p->dev_chunks.data(), p->dev_chunks.size() * 4);
+                        std::memcpy(s + L.xcd, p->xcd_tab, sizeof(p->xcd_tab));
+                        std::memcpy(s + L.gu_off, p->gu_off.data(), size_t(n_expert) * 8);
+                        std::memcpy(s + L.dn_off, p->dn_off.data(), size_t(n_expert) * 8);
+                    },
+                    [](hipStream_t) { return hipSuccess; });
+        if (st) {
             moe_plan_destroy(p);
-            return MOE_EHIP;
+            return st;
         }
-        uint8_t *s = static_cast<uint8_t *>(p->staging);
-        std::memset(s, 0, L.total);
-        std::memcpy(s + L.perm, p->perm.data(), size_t(R) * 4);
-        std::memcpy(s + L.inv, p->inv.data(), size_t(R) * 4);
-        std::memcpy(s + L.chunks, p->dev_chunks.data(), p->dev_chunks.size() * 4);
-        std::memcpy(s + L.xcd, p->xcd_tab, sizeof(p->xcd_tab));
-        std::memcpy(s + L.gu_off, p->gu_off.data(), size_t(n_expert) * 8);
-        std::memcpy(s + L.dn_off, p->dn_off.data(), size_t(n_expert) * 8);
-        hipStream_t hs = static_cast<hipStream_t>(stream);
-        if (hipEventCreateWithFlags(&p->uploaded, hipEventDisableTiming) != hipSuccess) {
-            p->uploaded = nullptr;
-            moe_plan_destroy(p);
-            return MOE_EHIP;
-        }
-        if (hipMemcpyAsync(plan_dev, s, L.total, hipMemcpyHostToDevice, hs) != hipSuccess ||
-            hipEventRecord(p->uploaded, hs) != hipSuccess) {
-            moe_plan_destroy(p);
-            return MOE_EHIP;
-        }
+    }
+    *out = p;
+    return MOE_OK;
+}
+
+int moe_prefill_plan_device(const int32_t *ids_dev, int tokens, int topk, int n_expert,
+                            int chunk_rows, const moe_weights *w_gu, const moe_weights *w_down,
+                            void *plan_dev, size_t plan_dev_bytes, void *stream, moe_plan **out) {
+    if (!out) return MOE_EINVAL;
+    *out = nullptr;
+    int st = check_plan_args(tokens, topk, n_expert, chunk_rows, w_gu, w_down);
+    if (st) return st;
+    if ((tokens > 0 && !ids_dev) || !plan_dev) return MOE_EINVAL;
+    if ((ids_dev && !aligned16(ids_dev)) || !aligned16(plan_dev)) return MOE_EALIGN;
+    const PlanLayout L = plan_layout(tokens, topk, n_expert, chunk_rows);
+    if (plan_dev_bytes < L.total) return MOE_ESIZE;
+    moe_plan *p = new_plan(tokens, topk, n_expert, chunk_rows, w_gu, w_down);
+    if (!p) return MOE_EINVAL;
+    p->device_built = true;
+    p->plan_dev = plan_dev;
+    // per-XCD list lengths are known only on the device: launches take the
+    // bound every list stays within, and the surplus workgroups exit at once
+    p->n_chunks = -1;
+    p->max_xcd_chunks = max_chunks(p->rows, n_expert, chunk_rows);
+    // the two weight offset tables go up from the host, the rest is built there
+    st = upload(p, L.gu_off, L.counts, stream,
+                [&](uint8_t *s) {
+                    std::memcpy(s + L.gu_off, p->gu_off.data(), size_t(n_expert) * 8);
+                    std::memcpy(s + L.dn_off, p->dn_off.data(), size_t(n_expert) * 8);
+                },
+                [&](hipStream_t hs) {
+                    return launch_device_plan(ids_dev, p->rows, n_expert, chunk_rows,
+                                              static_cast<uint8_t *>(plan_dev), L, hs);
+                });
+    if (st) {
+        moe_plan_destroy(p);
+        return st;
     }
     *out = p;
     return MOE_OK;
@@ -269,6 +346,32 @@ int moe_prefill_plan(const int32_t *ids, int tokens, int topk, int n_expert, int
 int moe_plan_query(const moe_plan *p, int *rows, int *n_chunks, int32_t *counts, int32_t *offsets,
                    int32_t *perm, int32_t *chunks) {
     if (!p) return MOE_EINVAL;
+    if (p->device_built) {
+        // read the device-built plan back (waits for it)
+        const int E = p->n_expert;
+        std::vector<int32_t> dc(E + 1), doff(E + 2), dperm(p->rows), status(1);
+        const uint8_t *ws = static_cast<const uint8_t *>(p->plan_dev);
+        const PlanLayout &L = p->layout;
+        if (hipEventSynchronize(p->uploaded) != hipSuccess ||
+            hipMemcpy(dc.data(), ws + L.counts, dc.size() * 4, hipMemcpyDeviceToHost) != hipSuccess ||
+            hipMemcpy(doff.data(), ws + L.offsets, doff.size() * 4, hipMemcpyDeviceToHost) != hipSuccess ||
+            hipMemcpy(status.data(), ws + L.aux + 4 * size_t(PlanAux::status(E)), 4,
+                      hipMemcpyDeviceToHost) != hipSuccess ||
+            (p->rows > 0 &&
+             hipMemcpy(dperm.data(), ws + L.perm, dperm.size() * 4, hipMemcpyDeviceToHost) != hipSuccess))
+            return MOE_EHIP;
+        if (status[0] != 0) return MOE_EINVAL;          // routing ids out of range
+        dc.resize(E);
+        doff.resize(E + 1);
+        const std::vector<int32_t> ch = chunk_list(expert_order(dc), dc, doff, p->chunk_rows);
+        if (rows) *rows = p->rows;
+        if (n_chunks) *n_chunks = int(ch.size() / 4);
+        if (counts) std::copy(dc.begin(), dc.end(), counts);
+        if (offsets) std::copy(doff.begin(), doff.end(), offsets);
+        if (perm) std::copy(dperm.begin(), dperm.end(), perm);
+        if (chunks) std::copy(ch.begin(), ch.end(), chunks);
+        return MOE_OK;
+    }
     if (rows) *rows = p->rows;
     if (n_chunks) *n_chunks = p->n_chunks;
     if (counts) std::copy(p->counts.begin(), p->counts.end(), counts);

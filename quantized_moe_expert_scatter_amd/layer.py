@@ -26,7 +26,8 @@ class DeviceLayer:
     """
 
     def __init__(self, x: np.ndarray, ids: np.ndarray, w_gu: ExpertWeights, w_down: ExpertWeights,
-                 chunk_rows: int = 128, device="cuda", stream=None, route_w: np.ndarray = None):
+                 chunk_rows: int = 128, device="cuda", stream=None, route_w: np.ndarray = None,
+                 device_plan: bool = False):
         import torch
         self.device = torch.device(device)
         self.tokens, self.hidden = x.shape
@@ -57,8 +58,16 @@ class DeviceLayer:
                                   if rw.size else np.zeros(4, np.float32), self.device)
         self.out = torch.empty((max(self.tokens, 1), self.hidden), dtype=torch.float32,
                                device=self.device)
-        self.plan = _lib.moe_prefill_plan(ids, self.n_expert, chunk_rows, self.w_gu, self.w_dn,
-                                          workspace=self.workspace, stream=stream)
+        if device_plan:
+            # the routing ids go up first and the plan is built from them on the GPU
+            self.ids_dev = _to_device(np.ascontiguousarray(ids, np.int32).reshape(-1)
+                                      if ids.size else np.zeros(4, np.int32), self.device)
+            self.plan = _lib.moe_prefill_plan_device(self.ids_dev, self.tokens, self.topk,
+                                                     self.n_expert, chunk_rows, self.w_gu,
+                                                     self.w_dn, self.workspace, stream)
+        else:
+            self.plan = _lib.moe_prefill_plan(ids, self.n_expert, chunk_rows, self.w_gu, self.w_dn,
+                                              workspace=self.workspace, stream=stream)
 
     def _packed(self, w: ExpertWeights, stream) -> "_lib.Weights":
         import torch

@@ -217,3 +217,31 @@ def test_pack_validation_errors():
     _, w_dn = _weights(cfg, tiled=False, down_type=2)
     w_dn.struct.codebook = None
     assert _pack_status(w_dn, DST, w_dn.struct.base_bytes) == -1
+
+
+def test_device_plan_validation_errors():
+    """moe_prefill_plan_device refuses, before any HIP call, what it can check
+    on the host (its routing ids are device memory, checked on the device)."""
+    L = _lib.lib()
+    cfg = wl.small_config("v", 8, 128, 64, 4, 2)
+    w_gu, w_dn = _weights(cfg)
+    need = _lib.moe_plan_device_bytes(8, 2, 4, 64)
+    DEV_IDS = 1 << 32
+
+    def st(ids=DEV_IDS, T=8, K=2, E=4, C=64, gu=w_gu, dn=w_dn, ws=FAKE_BASE, nb=need):
+        h = ctypes.c_void_p()
+        r = L.moe_prefill_plan_device(ids, T, K, E, C, ctypes.byref(gu.struct), ctypes.byref(dn.struct),
+                                      ws, nb, None, ctypes.byref(h))
+        assert h.value is None
+        return r
+
+    assert st(ws=None) == -1                      # the device workspace is required
+    assert st(ids=None) == -1
+    assert st(ids=DEV_IDS + 4) == -2
+    assert st(ws=FAKE_BASE + 8) == -2
+    assert st(nb=need - 16) == -4
+    assert st(C=0) == -1 and st(C=129) == -1 and st(K=0) == -1
+    u_gu, _ = _weights(cfg, tiled=False)
+    assert st(gu=u_gu) == -3
+    assert L.moe_prefill_plan_device(DEV_IDS, 8, 2, 4, 64, ctypes.byref(w_gu.struct),
+                                     ctypes.byref(w_dn.struct), FAKE_BASE, need, None, None) == -1
