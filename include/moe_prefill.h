@@ -170,6 +170,7 @@ int moe_prefill_plan(const int32_t *ids_host, int tokens, int topk, int n_expert
  *              enqueued on `stream` (it must stay valid until they ran).
  *   plan_dev   required.  Every section the kernels read holds the same bytes
  *              as a host-built plan of the same ids.
+ *   n_expert   at most 2048, and tokens*topk below 2^29 (MOE_EINVAL beyond).
  * Nothing is read back: the call enqueues a host-to-device copy of the two
  * weight offset tables and five small integer kernels (clear; count; prefix,
  * expert ranking and XCD dealing in one workgroup; a stable ballot compaction

@@ -36,6 +36,10 @@ struct PlanLayout {
     size_t total;
 };
 
+// Experts a device-built plan takes (its scheduling workgroup stages four
+// int32 arrays of this length in LDS, 32 KB).
+constexpr int kPlanMaxExperts = 2048;
+
 // Scratch of the device-built plan, int32 indices into the aux section.
 struct PlanAux {
     static constexpr int order(int e) { return e; }                        // experts by rank

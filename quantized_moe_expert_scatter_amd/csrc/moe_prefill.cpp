@@ -313,7 +313,9 @@ int moe_prefill_plan_device(const int32_t *ids_dev, int tokens, int topk, int n_
     *out = nullptr;
     int st = check_plan_args(tokens, topk, n_expert, chunk_rows, w_gu, w_down);
     if (st) return st;
-    if ((tokens > 0 && !ids_dev) || !plan_dev) return MOE_EINVAL;
+    if ((tokens > 0 && !ids_dev) || !plan_dev || n_expert > kPlanMaxExperts) return MOE_EINVAL;
+    // the dealing packs an XCD's rows and its index into 32 bits
+    if ((long long)tokens * topk >= (1LL << 29)) return MOE_EINVAL;
     if ((ids_dev && !aligned16(ids_dev)) || !aligned16(plan_dev)) return MOE_EALIGN;
     const PlanLayout L = plan_layout(tokens, topk, n_expert, chunk_rows);
     if (plan_dev_bytes < L.total) return MOE_ESIZE;

@@ -10,8 +10,8 @@
 //             goes to an extra bucket E, which no product reads, and is
 //             reported by the plan query;
 //   3. one workgroup: offsets (exclusive prefix), experts ranked by row count
-//             (ties by id), dealt largest first to the XCD with the fewest
-//             rows so far, and each XCD's list start and length;
+//             (ties by id) with a bitonic sort, dealt largest first to the XCD
+//             with the fewest rows so far, each XCD's list start and length;
 //   4. one workgroup per bucket: the bucket's rows in ascending t*K+k order by
 //             a ballot compaction over all ids (stable, no atomics), writing
 //             perm and its inverse;
@@ -26,6 +26,7 @@ namespace moe {
 namespace {
 
 constexpr int kPlanThreads = 256;
+static_assert(kXcds == 8, "the dealing's argmin tree assumes eight XCDs");
 
 // Zeroes the counters, the chunk table and the alignment padding after perm
 // and inv (a host-built plan's upload zeroes them too).
@@ -42,79 +43,156 @@ __global__ __launch_bounds__(kPlanThreads) void plan_clear_kernel(int32_t *count
     }
 }
 
+// Rows per bucket: each workgroup counts 2048 ids into LDS bins, then adds
+// its non-zero bins to the global counts (integer atomics: the totals do not
+// depend on the order).
 __global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(const int32_t *ids, int rows,
                                                                   int n_expert, int32_t *counts) {
-    const int i = blockIdx.x * kPlanThreads + threadIdx.x;
-    if (i >= rows) return;
-    int e = ids[i];
-    if (e < 0 || e >= n_expert) e = n_expert;
-    atomicAdd(&counts[e], 1);
+    constexpr int kPer = 8;
+    __shared__ int32_t bins[kPlanMaxExperts + 1];
+    const int tid = threadIdx.x;
+    for (int e = tid; e <= n_expert; e += kPlanThreads) bins[e] = 0;
+    __syncthreads();
+    const int first = (blockIdx.x * kPlanThreads + tid) * kPer;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+        if (first + j < rows) {
+            int e = ids[first + j];
+            if (e < 0 || e >= n_expert) e = n_expert;
+            atomicAdd(&bins[e], 1);
+        }
+    __syncthreads();
+    for (int e = tid; e <= n_expert; e += kPlanThreads)
+        if (bins[e]) atomicAdd(&counts[e], bins[e]);
 }
 
-// One workgroup.  Thread 0 does the two sequential passes (the prefix over
-// E + 1 buckets and the greedy dealing, E steps each); the O(E^2) ranking is
-// spread over the threads.
+// One workgroup on the counts staged in LDS: the offsets by a parallel
+// prefix, the ranking by a bitonic sort, then the greedy dealing, which is
+// sequential in rank order: wave 0 runs it on rows and chunk counts gathered
+// in rank order beforehand, and the results go back to memory in parallel.
 __global__ __launch_bounds__(kPlanThreads) void plan_schedule_kernel(const int32_t *counts,
                                                                      int n_expert, int chunk_rows,
                                                                      int32_t *offsets, int32_t *aux,
                                                                      int32_t *xcd_tab) {
+    __shared__ int32_t s_counts[kPlanMaxExperts + 1];
+    __shared__ uint64_t s_key[kPlanMaxExperts];     // (rows descending, id) sort keys
+    __shared__ int32_t s_rows[kPlanMaxExperts];     // rows of the expert of rank r, then its XCD
+    __shared__ int32_t s_base[kPlanMaxExperts];     // its first slot in that XCD's list
+    __shared__ int32_t s_wave[kPlanThreads / 64];
+    __shared__ int32_t s_listed[kXcds];
     const int tid = threadIdx.x;
-    if (tid == 0) {
-        int32_t run = 0;
-        for (int b = 0; b <= n_expert; ++b) {
-            offsets[b] = run;
-            run += counts[b];
-        }
-        offsets[n_expert + 1] = run;
-        aux[PlanAux::status(n_expert)] = counts[n_expert];
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int nb = n_expert + 1;
+    for (int b = tid; b < nb; b += kPlanThreads) s_counts[b] = counts[b];
+    __syncthreads();
+
+    // offsets: each thread a contiguous segment of buckets
+    const int seg = (nb + kPlanThreads - 1) / kPlanThreads;
+    const int lo = min(nb, tid * seg), hi = min(nb, lo + seg);
+    int32_t local = 0;
+    for (int b = lo; b < hi; ++b) local += s_counts[b];
+    int32_t incl = local;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int32_t up = __shfl_up(incl, d, 64);
+        incl += lane >= d ? up : 0;
     }
-    // rank of expert e: experts with more rows, or as many rows and a lower id
-    for (int e = tid; e < n_expert; e += kPlanThreads) {
-        const int32_t c = counts[e];
-        int rank = 0;
-        for (int f = 0; f < n_expert; ++f) {
-            const int32_t cf = counts[f];
-            rank += (cf > c || (cf == c && f < e)) ? 1 : 0;
+    if (lane == 63) s_wave[wave] = incl;
+    // experts ranked by rows descending, then id: a bitonic sort of the keys
+    // (2^31 - 1 - rows) << 32 | id, padded to a power of two with the largest key
+    int np2 = 1;
+    while (np2 < n_expert) np2 <<= 1;
+    for (int e = tid; e < np2; e += kPlanThreads)
+        s_key[e] = e < n_expert ? (uint64_t(0x7FFFFFFFu - uint32_t(s_counts[e])) << 32) | uint32_t(e)
+                                : ~0ull;
+    __syncthreads();
+    for (int k = 2; k <= np2; k <<= 1)
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = tid; i < np2; i += kPlanThreads) {
+                const int ixj = i ^ j;
+                if (ixj > i) {
+                    const uint64_t a = s_key[i], b = s_key[ixj];
+                    if ((a > b) == ((i & k) == 0)) {
+                        s_key[i] = b;
+                        s_key[ixj] = a;
+                    }
+                }
+            }
+            __syncthreads();
         }
-        aux[PlanAux::order(rank)] = e;
+    int32_t run = incl - local;
+    for (int w = 0; w < wave; ++w) run += s_wave[w];
+    for (int b = lo; b < hi; ++b) {
+        offsets[b] = run;
+        run += s_counts[b];
+    }
+    if (tid == kPlanThreads - 1) offsets[nb] = run;
+    if (tid == 0) aux[PlanAux::status(n_expert)] = s_counts[n_expert];
+    for (int r = tid; r < n_expert; r += kPlanThreads) s_rows[r] = s_counts[uint32_t(s_key[r])];
+    __syncthreads();
+
+    if (wave == 0) {
+        // lane x < 8 holds XCD x's rows so far and its list length; a step
+        // takes the first XCD of least rows as the least (rows << 3 | x) key
+        // of lanes 0..7, by three DPP shifts of a prefix minimum
+        uint32_t load = lane < kXcds ? 0u : 0x1FFFFFFFu;
+        int32_t listed = 0;
+        for (int r0 = 0; r0 < n_expert; r0 += 64) {
+            const int n = min(64, n_expert - r0);
+            const int32_t cvec = lane < n ? s_rows[r0 + lane] : 0;
+            const int32_t nvec = (cvec + chunk_rows - 1) / chunk_rows;
+            int32_t xs = -1, bases = 0;
+            for (int j = 0; j < n; ++j) {
+                const int32_t c = __builtin_amdgcn_readlane(cvec, j);
+                if (c == 0) break;                  // ranks past here have no rows
+                uint32_t key = (load << 3) | uint32_t(lane & 7);
+                key = min(key, uint32_t(__builtin_amdgcn_update_dpp(int(key), int(key), 0x111, 0xF, 0xF, false)));
+                key = min(key, uint32_t(__builtin_amdgcn_update_dpp(int(key), int(key), 0x112, 0xF, 0xF, false)));
+                key = min(key, uint32_t(__builtin_amdgcn_update_dpp(int(key), int(key), 0x114, 0xF, 0xF, false)));
+                const int x = __builtin_amdgcn_readlane(int(key), 7) & 7;
+                const int32_t base = __builtin_amdgcn_readlane(listed, x);
+                const int32_t nch = __builtin_amdgcn_readlane(nvec, j);
+                const bool mine = lane == x;            // no branch: both adds run
+                load += mine ? uint32_t(c) : 0u;
+                listed += mine ? nch : 0;
+                xs = lane == j ? x : xs;
+                bases = lane == j ? base : bases;
+            }
+            if (lane < n) {
+                s_rows[r0 + lane] = cvec == 0 ? -1 : xs;
+                s_base[r0 + lane] = cvec == 0 ? 0 : bases;
+            }
+        }
+        if (lane < kXcds) s_listed[lane] = listed;
     }
     __syncthreads();
+    for (int r = tid; r < n_expert; r += kPlanThreads) {
+        const int e = int(uint32_t(s_key[r]));
+        aux[PlanAux::order(r)] = e;
+        aux[PlanAux::xcd_of(n_expert, e)] = s_rows[r];
+        aux[PlanAux::base_of(n_expert, e)] = s_base[r];
+    }
     if (tid == 0) {
-        long long load[kXcds] = {};
-        int32_t listed[kXcds] = {};
-        for (int r = 0; r < n_expert; ++r) {
-            const int e = aux[PlanAux::order(r)];
-            const int32_t c = counts[e];
-            if (c == 0) {
-                aux[PlanAux::xcd_of(n_expert, e)] = -1;
-                aux[PlanAux::base_of(n_expert, e)] = 0;
-                continue;
-            }
-            int x = 0;
-            for (int k = 1; k < kXcds; ++k)
-                if (load[k] < load[x]) x = k;
-            load[x] += c;
-            aux[PlanAux::xcd_of(n_expert, e)] = x;
-            aux[PlanAux::base_of(n_expert, e)] = listed[x];
-            listed[x] += (c + chunk_rows - 1) / chunk_rows;
-        }
         int32_t start = 0;
         for (int x = 0; x < kXcds; ++x) {
             xcd_tab[x] = start;
-            xcd_tab[kXcds + x] = listed[x];
-            start += listed[x];
+            xcd_tab[kXcds + x] = s_listed[x];
+            start += s_listed[x];
         }
     }
 }
 
 // Workgroup b collects the rows of bucket b (expert b, or the out-of-range ids
-// for b == E) in ascending index order: each pass over 256 ids ranks the
-// matches by a wave ballot and the waves' totals.
+// for b == E) in ascending index order.  Each pass covers 2048 ids, eight
+// consecutive ones per thread: a thread's matches are numbered after those of
+// the threads before it (a wave prefix sum by shuffles, then the waves' totals).
 __global__ __launch_bounds__(kPlanThreads) void plan_scatter_kernel(const int32_t *ids, int rows,
                                                                     int n_expert,
                                                                     const int32_t *counts,
                                                                     const int32_t *offsets,
                                                                     int32_t *perm, int32_t *inv) {
+    constexpr int kPer = 8;
     __shared__ int32_t wave_total[kPlanThreads / 64];
     const int b = blockIdx.x;
     const int32_t cnt = counts[b];
@@ -123,18 +201,34 @@ __global__ __launch_bounds__(kPlanThreads) void plan_scatter_kernel(const int32_
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
     int32_t found = 0;
-    for (int i0 = 0; i0 < rows && found < cnt; i0 += kPlanThreads) {
-        const int i = i0 + tid;
-        bool match = false;
-        if (i < rows) {
-            int e = ids[i];
-            if (e < 0 || e >= n_expert) e = n_expert;
-            match = e == b;
+    for (int i0 = 0; i0 < rows && found < cnt; i0 += kPer * kPlanThreads) {
+        const int first = i0 + kPer * tid;
+        int e[kPer];
+        if (first + kPer <= rows) {
+            const int4 v0 = *reinterpret_cast<const int4 *>(ids + first);
+            const int4 v1 = *reinterpret_cast<const int4 *>(ids + first + 4);
+            e[0] = v0.x; e[1] = v0.y; e[2] = v0.z; e[3] = v0.w;
+            e[4] = v1.x; e[5] = v1.y; e[6] = v1.z; e[7] = v1.w;
+        } else {
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) e[j] = first + j < rows ? ids[first + j] : -1;
         }
-        const uint64_t mask = __ballot(match);
-        if (lane == 0) wave_total[wave] = __popcll(mask);
+        unsigned bits = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            int ej = e[j];
+            if (ej < 0 || ej >= n_expert) ej = n_expert;
+            bits |= (first + j < rows && ej == b) ? (1u << j) : 0u;
+        }
+        const int mine = __popc(bits);
+        int incl = mine;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int up = __shfl_up(incl, d, 64);
+            incl += lane >= d ? up : 0;
+        }
+        if (lane == 63) wave_total[wave] = incl;
         __syncthreads();
         int32_t before = 0, total = 0;
 #pragma unroll
@@ -142,13 +236,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_scatter_kernel(const int32_
             before += w < wave ? wave_total[w] : 0;
             total += wave_total[w];
         }
-        if (match) {
-            const int32_t pos = found + before + __popcll(mask & below);
-            if (pos < cnt) {
-                perm[base + pos] = i;
-                inv[i] = base + pos;
+        int32_t pos = found + before + incl - mine;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            if (bits & (1u << j)) {
+                if (pos < cnt) {
+                    perm[base + pos] = first + j;
+                    inv[first + j] = base + pos;
+                }
+                ++pos;
             }
-        }
         found += total;
         __syncthreads();          // wave_total is rewritten by the next pass
     }
@@ -193,8 +290,8 @@ hipError_t launch_device_plan(const int32_t *ids, int rows, int n_expert, int ch
     hipLaunchKernelGGL(plan_clear_kernel, dim3(blocks_for(n_clear)), dim3(kPlanThreads), 0, stream,
                        counts, n_expert + 1, chunks, 4 * maxc, perm + rows, inv + rows, n_pad);
     if (rows > 0)
-        hipLaunchKernelGGL(plan_count_kernel, dim3(blocks_for(rows)), dim3(kPlanThreads), 0, stream,
-                           ids, rows, n_expert, counts);
+        hipLaunchKernelGGL(plan_count_kernel, dim3(blocks_for((rows + 7) / 8)), dim3(kPlanThreads), 0,
+                           stream, ids, rows, n_expert, counts);
     hipLaunchKernelGGL(plan_schedule_kernel, dim3(1), dim3(kPlanThreads), 0, stream, counts, n_expert,
                        chunk_rows, offsets, aux, xcd);
     if (rows > 0)
