@@ -44,6 +44,7 @@ KERNEL_SOURCES = {
     "expert_down": "quantized_moe_expert_scatter_amd/csrc/expert_kernels.hip",
     "quantize_scatter": "quantized_moe_expert_scatter_amd/csrc/quant_kernels.hip",
     "swiglu_q8": "quantized_moe_expert_scatter_amd/csrc/quant_kernels.hip",
+    "moe_combine": "quantized_moe_expert_scatter_amd/csrc/combine_kernels.hip",
 }
 
 
