@@ -79,7 +79,12 @@ typedef enum {
     MOE_ESTATE = -6    /* the plan was built without a device workspace */
 } moe_status;
 
-typedef enum { MOE_W_Q2_0 = 1, MOE_W_NL4 = 2, MOE_W_TILED = 0x100 } moe_wtype;
+typedef enum {
+    MOE_W_Q2_0 = 1,
+    MOE_W_NL4 = 2,
+    MOE_W_TILED = 0x100,           /* the kernels' layout, written by moe_weights_pack */
+    MOE_W_GU_INTERLEAVED = 0x200   /* gate/up rows alternate: row 2j gate j, 2j+1 up j */
+} moe_wtype;
 
 /* The weights of one product (gate/up or down) for all experts of a layer,
  * read in place: expert e's matrix starts at base + offset[e] ("Strata"
@@ -125,6 +130,10 @@ size_t moe_weight_bytes(int type, int rows, int cols);
  * dst_bytes, same offsets} then describes the packed weights.  A pure byte
  * permutation inside each plane, done once when a layer is loaded (one launch
  * when the experts sit at a constant stride, else one per expert).
+ * Gate/up weights stored with alternating rows (type | MOE_W_GU_INTERLEAVED,
+ * the other row order the pages' swiglu_quant test covers) are packed into
+ * split order, gate rows first; the packed descriptor does not carry the flag
+ * (the plan refuses it).
  *   dst        device buffer, 16-byte aligned, every expert inside dst_bytes,
  *              not overlapping w->base's buffer; owned by the caller.
  * Experts must share a matrix (equal offsets) or not overlap.  Asynchronous

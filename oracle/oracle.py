@@ -263,11 +263,15 @@ def combine(dm: np.ndarray, w: np.ndarray) -> np.ndarray:
     return out
 
 
-def layer(x, ids, n_expert, n_ff, w_gu, w_down, chunk_rows: int = 64, n_threads: int = 1) -> LayerResult:
+def layer(x, ids, n_expert, n_ff, w_gu, w_down, chunk_rows: int = 64, n_threads: int = 1,
+          gu_interleaved: bool = False) -> LayerResult:
     """The whole routed-expert product of one layer, step by step.
 
     w_gu / w_down: (wtype, buf, offsets, codebook) of the gate/up product
-    [2*n_ff, hidden] and the down product [hidden, n_ff]."""
+    [2*n_ff, hidden] and the down product [hidden, n_ff].  gu_interleaved:
+    the gate/up rows alternate (row 2j gate j, row 2j+1 up j), so GU does too
+    and swiglu reads it that way ("Strata" PR #3752, swiglu_quant commit: its
+    test covers split and interleaved gate/up rows)."""
     T, H = x.shape
     K = ids.shape[1]
     pl = plan(ids, n_expert, chunk_rows)
@@ -275,7 +279,7 @@ def layer(x, ids, n_expert, n_ff, w_gu, w_down, chunk_rows: int = 64, n_threads:
     xq = quantize_scatter(x, K, pl.perm)
     gu = expert_product(w_gu[0], w_gu[1], w_gu[2], n_expert, 2 * n_ff, H, w_gu[3], xq, row_e,
                         n_threads=n_threads)
-    hq = swiglu_q8(gu, n_ff)
+    hq = swiglu_q8(gu, n_ff, interleaved=gu_interleaved)
     d_sorted = expert_product(w_down[0], w_down[1], w_down[2], n_expert, H, n_ff, w_down[3], hq,
                               row_e, n_threads=n_threads)
     dm = np.zeros((T * K, H), np.float32)

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_prefill.so")
 MOE_W_Q2_0 = 1
 MOE_W_NL4 = 2
 MOE_W_TILED = 0x100
+MOE_W_GU_INTERLEAVED = 0x200
 
 STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EALIGN", -3: "MOE_EFORMAT",
           -4: "MOE_ESIZE", -5: "MOE_EHIP", -6: "MOE_ESTATE"}
@@ -150,8 +151,8 @@ def moe_weights_pack(w: Weights, dst, stream=None) -> Weights:
     _check(lib().moe_weights_pack(ctypes.byref(w.struct), _ptr(dst), nbytes, _stream(stream)),
            "moe_weights_pack")
     s = w.struct
-    return Weights(s.type | MOE_W_TILED, s.rows, s.cols, s.n_expert, dst, nbytes, w.offsets,
-                   w.codebook)
+    return Weights((s.type & ~MOE_W_GU_INTERLEAVED) | MOE_W_TILED, s.rows, s.cols, s.n_expert,
+                   dst, nbytes, w.offsets, w.codebook)
 
 
 class Plan:

@@ -102,8 +102,11 @@ hipError_t launch_device_plan(const int32_t *ids, int rows, int n_expert, int ch
 hipError_t launch_combine(const float *dm, const float *w, int tokens, int topk, int hidden,
                           float *out, hipStream_t stream);
 // Packs n_expert matrices of rows x blocks_per_row blocks into the tiled
-// layout; expert e's planes start at src/dst + e * expert_stride.
+// layout; expert e's planes start at src/dst + e * expert_stride.  half > 0:
+// the source rows alternate gate/up (2j gate j, 2j+1 up j, j < half) and the
+// packed rows are in split order.
 hipError_t launch_weight_pack(const uint8_t *src, uint8_t *dst, uint64_t expert_stride,
-                              int n_expert, int rows, int blocks_per_row, hipStream_t stream);
+                              int n_expert, int rows, int blocks_per_row, int half,
+                              hipStream_t stream);
 
 }  // namespace moe

@@ -39,8 +39,8 @@ namespace {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// the block format of a weight type, with or without the MOE_W_TILED flag
-int base_type(int type) { return type & ~int(MOE_W_TILED); }
+// the block format of a weight type, without the layout flags
+int base_type(int type) { return type & ~int(MOE_W_TILED | MOE_W_GU_INTERLEAVED); }
 
 int block_values(int type) {
     const int t = base_type(type);
@@ -60,6 +60,8 @@ int check_weights(const moe_weights *w, int n_expert, bool tiled) {
     const int t = base_type(w->type);
     if (t != MOE_W_Q2_0 && t != MOE_W_NL4) return MOE_EFORMAT;
     if (((w->type & MOE_W_TILED) != 0) != tiled) return MOE_EFORMAT;
+    // alternating gate/up rows are a storage order the pack undoes
+    if (tiled && (w->type & MOE_W_GU_INTERLEAVED)) return MOE_EFORMAT;
     if (w->n_expert != n_expert || w->rows <= 0 || w->cols <= 0) return MOE_EINVAL;
     if (w->rows % 64 || w->cols % block_values(t)) return MOE_EFORMAT;
     if (t == MOE_W_NL4 && !w->codebook) return MOE_EINVAL;
@@ -185,6 +187,7 @@ int moe_weights_pack(const moe_weights *w, void *dst, size_t dst_bytes, void *st
     const auto *src = static_cast<const uint8_t *>(w->base);
     auto *out = static_cast<uint8_t *>(dst);
     const int nb = w->cols / block_values(w->type);
+    const int half = (w->type & MOE_W_GU_INTERLEAVED) ? w->rows / 2 : 0;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     // experts at a constant stride go in one launch, others one launch each
     bool uniform = w->n_expert <= 65535;
@@ -193,9 +196,10 @@ int moe_weights_pack(const moe_weights *w, void *dst, size_t dst_bytes, void *st
         uniform = w->offset[e] >= w->offset[0] && w->offset[e] - w->offset[0] == uint64_t(e) * stride;
     if (uniform)
         return hip_status(launch_weight_pack(src + w->offset[0], out + w->offset[0], stride,
-                                             stride ? w->n_expert : 1, w->rows, nb, s));
+                                             stride ? w->n_expert : 1, w->rows, nb, half, s));
     for (int e = 0; e < w->n_expert; ++e) {
-        const hipError_t err = launch_weight_pack(src + w->offset[e], out + w->offset[e], 0, 1, w->rows, nb, s);
+        const hipError_t err =
+            launch_weight_pack(src + w->offset[e], out + w->offset[e], 0, 1, w->rows, nb, half, s);
         if (err != hipSuccess) return MOE_EHIP;
     }
     return MOE_OK;

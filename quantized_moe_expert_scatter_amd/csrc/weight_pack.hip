@@ -19,11 +19,12 @@ namespace moe {
 namespace {
 
 // One thread per block slot of the packed order: slot d is (tile i, block b,
-// row r) with d = (i * nb + b) * 32 + r, filled from block b of row 32 i + r.
-// Writes are contiguous in d; reads gather 16-byte blocks.
+// row r) with d = (i * nb + b) * 32 + r, filled from block b of row 32 i + r
+// (of row 2n or 2(n - half) + 1 for packed row n when the source alternates
+// gate and up rows).  Writes are contiguous in d; reads gather 16-byte blocks.
 __global__ __launch_bounds__(256) void weight_pack_kernel(const uint8_t *src, uint8_t *dst,
                                                           uint64_t expert_stride, uint32_t n_blocks,
-                                                          uint32_t nb) {
+                                                          uint32_t nb, uint32_t half) {
     const uint32_t d = blockIdx.x * 256u + threadIdx.x;
     if (d >= n_blocks) return;
     const uint64_t e = uint64_t(blockIdx.y) * expert_stride;
@@ -33,7 +34,9 @@ __global__ __launch_bounds__(256) void weight_pack_kernel(const uint8_t *src, ui
     const uint32_t q = d >> 5;
     const uint32_t b = q % nb;
     const uint32_t i = q / nb;
-    const uint32_t s = (32u * i + r) * nb + b;
+    const uint32_t row = 32u * i + r;
+    const uint32_t src_row = half == 0 ? row : (row < half ? 2u * row : 2u * (row - half) + 1u);
+    const uint32_t s = src_row * nb + b;
     *reinterpret_cast<uint4 *>(d_codes + size_t(d) * 16) =
         *reinterpret_cast<const uint4 *>(s_codes + size_t(s) * 16);
     const uint16_t *s_scales = reinterpret_cast<const uint16_t *>(s_codes + size_t(n_blocks) * 16);
@@ -44,12 +47,13 @@ __global__ __launch_bounds__(256) void weight_pack_kernel(const uint8_t *src, ui
 }  // namespace
 
 hipError_t launch_weight_pack(const uint8_t *src, uint8_t *dst, uint64_t expert_stride,
-                              int n_expert, int rows, int blocks_per_row, hipStream_t stream) {
+                              int n_expert, int rows, int blocks_per_row, int half,
+                              hipStream_t stream) {
     const uint32_t n_blocks = uint32_t(rows) * uint32_t(blocks_per_row);
     if (n_blocks == 0 || n_expert <= 0) return hipSuccess;
     const dim3 grid((n_blocks + 255u) / 256u, uint32_t(n_expert)), block(256);
     hipLaunchKernelGGL(weight_pack_kernel, grid, block, 0, stream, src, dst, expert_stride, n_blocks,
-                       uint32_t(blocks_per_row));
+                       uint32_t(blocks_per_row), uint32_t(half));
     return hipGetLastError();
 }
 

@@ -27,7 +27,7 @@ class DeviceLayer:
 
     def __init__(self, x: np.ndarray, ids: np.ndarray, w_gu: ExpertWeights, w_down: ExpertWeights,
                  chunk_rows: int = 128, device="cuda", stream=None, route_w: np.ndarray = None,
-                 device_plan: bool = False):
+                 device_plan: bool = False, gu_interleaved: bool = False):
         import torch
         self.device = torch.device(device)
         self.tokens, self.hidden = x.shape
@@ -39,7 +39,7 @@ class DeviceLayer:
         self.x = _to_device(x.astype(np.float32, copy=False), self.device)
         # weights arrive as row-major planes and are packed once into the
         # kernels' tiled layout; the row-major copies are dropped after that
-        self.w_gu = self._packed(w_gu, stream)
+        self.w_gu = self._packed(w_gu, stream, _lib.MOE_W_GU_INTERLEAVED if gu_interleaved else 0)
         self.w_dn = self._packed(w_down, stream)
         u8 = torch.uint8
         ws = _lib.moe_plan_device_bytes(self.tokens, self.topk, self.n_expert, chunk_rows)
@@ -69,10 +69,10 @@ class DeviceLayer:
             self.plan = _lib.moe_prefill_plan(ids, self.n_expert, chunk_rows, self.w_gu, self.w_dn,
                                               workspace=self.workspace, stream=stream)
 
-    def _packed(self, w: ExpertWeights, stream) -> "_lib.Weights":
+    def _packed(self, w: ExpertWeights, stream, flags: int = 0) -> "_lib.Weights":
         import torch
         raw = _to_device(w.buf, self.device)
-        rw = _lib.Weights(w.wtype, w.rows, w.cols, w.n_expert, raw, w.buf.nbytes, w.offsets,
+        rw = _lib.Weights(w.wtype | flags, w.rows, w.cols, w.n_expert, raw, w.buf.nbytes, w.offsets,
                           w.codebook)
         dst = torch.empty_like(raw)
         packed = _lib.moe_weights_pack(rw, dst, stream)

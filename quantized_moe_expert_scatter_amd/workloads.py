@@ -256,6 +256,25 @@ def expert_weights(wtype: int, rows: int, cols: int, n_expert: int, seed: int,
     return ExpertWeights(wtype, rows, cols, n_expert, buf, offsets, codebook)
 
 
+def interleave_gate_up(w: ExpertWeights) -> ExpertWeights:
+    """The same gate/up matrices stored with alternating rows: row 2j is gate
+    row j, row 2j+1 up row j (both planes), same offsets."""
+    F = w.rows // 2
+    nb = w.cols // block_of(w.wtype)
+    n = w.rows * nb
+    order = np.empty(w.rows, np.int64)
+    order[0::2] = np.arange(F)
+    order[1::2] = F + np.arange(F)
+    buf = w.buf.copy()
+    for e in range(w.n_expert):
+        o = int(w.offsets[e])
+        codes = w.buf[o:o + 16 * n].reshape(w.rows, nb * 16)
+        scales = w.buf[o + 16 * n:o + 18 * n].reshape(w.rows, nb * 2)
+        buf[o:o + 16 * n] = codes[order].reshape(-1)
+        buf[o + 16 * n:o + 18 * n] = scales[order].reshape(-1)
+    return ExpertWeights(w.wtype, w.rows, w.cols, w.n_expert, buf, w.offsets.copy(), w.codebook)
+
+
 # ----------------------------------------------------------------------- layer
 @dataclass
 class Layer:

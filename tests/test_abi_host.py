@@ -136,6 +136,9 @@ def test_validation_errors():
         ws = list(_weights(cfg))
         ws[which].struct.type &= ~_lib.MOE_W_TILED
         assert _plan_status(ids, 4, 64, *ws) == -3
+    ws = list(_weights(cfg))                   # alternating gate/up rows must be packed first
+    ws[0].struct.type |= _lib.MOE_W_GU_INTERLEAVED
+    assert _plan_status(ids, 4, 64, *ws) == -3
     w_gu, w_dn = _weights(cfg)
     w_gu.struct.type = 2 | _lib.MOE_W_TILED    # NL4 gate/up needs its codebook
     assert _plan_status(ids, 4, 64, w_gu, w_dn) == -1

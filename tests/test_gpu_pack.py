@@ -48,3 +48,22 @@ def test_pack_is_the_tiled_permutation(wtype, rows, cols, E, shuffle):
         expect[o:o + 16 * n] = _tiled(m[:16 * n], rows, nb, 16)
         expect[o + 16 * n:o + 18 * n] = _tiled(m[16 * n:], rows, nb, 2)
     assert np.array_equal(out, expect)
+
+
+@pytest.mark.parametrize("wtype,rows,cols,E", [(wl.Q2_0, 128, 192, 3), (wl.NL4, 192, 96, 2)])
+def test_pack_deinterleaves_gate_up(wtype, rows, cols, E):
+    """Alternating gate/up rows are packed into split order: the result equals
+    packing the split-stored matrices."""
+    print(f"case interleaved wtype={wtype} rows={rows} cols={cols} E={E}", flush=True)
+    w = wl.expert_weights(wtype, rows, cols, E, seed=rows + 7)
+    wi = wl.interleave_gate_up(w)
+    outs = []
+    for ww, flag in ((w, 0), (wi, _lib.MOE_W_GU_INTERLEAVED)):
+        src = torch.from_numpy(ww.buf).cuda()
+        rw = _lib.Weights(ww.wtype | flag, rows, cols, E, src, ww.buf.nbytes, ww.offsets, ww.codebook)
+        dst = torch.zeros_like(src)
+        packed = _lib.moe_weights_pack(rw, dst)
+        torch.cuda.synchronize()
+        assert packed.struct.type == wtype | _lib.MOE_W_TILED
+        outs.append(dst.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])

@@ -20,6 +20,7 @@ import torch
 from oracle import oracle
 from quantized_moe_expert_scatter_amd import _lib
 from quantized_moe_expert_scatter_amd import workloads as wl
+from quantized_moe_expert_scatter_amd.layer import DeviceLayer
 from tests.gpu_common import (check_expert_outputs, device_layer, flip_rows, oracle_rows,
                               rel_rms, w_tuple)
 
@@ -239,6 +240,30 @@ def test_combine(name):
     e = rel_rms(out, oracle.combine(ref.dm, L.route_w))
     assert e <= 1e-2 if flip_rows(D.hq_host(), ref.hq).size else e <= 1e-5, e
     D.close()
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged", "nl4_gu"])
+def test_interleaved_gate_up_rows(name):
+    """Gate/up weights stored with alternating rows give the bytes of the
+    split-stored layer, and match the oracle run on the alternating rows with
+    its interleaved swiglu."""
+    L = _small_layer(name)
+    _say("case", name)
+    Li = wl.interleave_gate_up(L.w_gu)
+    cfg = L.cfg
+    ref = oracle.layer(L.x, L.ids, cfg.n_expert, cfg.n_ff, w_tuple(Li), w_tuple(L.w_down),
+                       n_threads=8, gu_interleaved=True)
+    A = device_layer(L)
+    B = DeviceLayer(L.x, L.ids, Li, L.w_down, chunk_rows=64, route_w=L.route_w, gu_interleaved=True)
+    for D in (A, B):
+        D.run_fused()
+    torch.cuda.synchronize()
+    assert torch.equal(A.hq, B.hq) and torch.equal(A.dm.view(torch.int32), B.dm.view(torch.int32))
+    flips = flip_rows(B.hq_host(), ref.hq)
+    assert flips.size <= max(2, cfg.rows // 100)
+    check_expert_outputs(B.dm_host(), ref.dm, ref.plan.perm[flips], name)
+    A.close()
+    B.close()
 
 
 # ------------------------------------------------------------- full layers

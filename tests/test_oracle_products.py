@@ -161,3 +161,22 @@ def test_chain_against_fp64_dequantized(which):
     # is [2e-3, 3e-2] for the whole chain
     assert 2e-3 <= e_dm <= 3e-2, e_dm
     assert 1e-3 <= e_gu <= 3e-2, e_gu
+
+
+def test_interleaved_gate_up_rows_reduce_to_split():
+    """The oracle's interleaved option on alternating gate/up rows is the
+    split layer with GU's columns interleaved: same GU values, same Hq and Dm
+    bytes (the two row orders the pages' swiglu_quant test covers)."""
+    L = wl.make_layer(wl.small_config("il", 30, 256, 128, 4, 2, seed=5))
+    Li = wl.interleave_gate_up(L.w_gu)
+    cfg = L.cfg
+    F = cfg.n_ff
+
+    def wt(w):
+        return (w.wtype, w.buf, w.offsets, w.codebook)
+
+    a = oracle.layer(L.x, L.ids, cfg.n_expert, F, wt(L.w_gu), wt(L.w_down))
+    b = oracle.layer(L.x, L.ids, cfg.n_expert, F, wt(Li), wt(L.w_down), gu_interleaved=True)
+    assert np.array_equal(b.gu[:, 0::2], a.gu[:, :F]) and np.array_equal(b.gu[:, 1::2], a.gu[:, F:])
+    assert np.array_equal(a.hq, b.hq)
+    assert np.array_equal(a.dm.view(np.uint32), b.dm.view(np.uint32))
