@@ -1,0 +1,298 @@
+// expert_small_kernels.hip -- the expert products for chunks of a few rows.
+//
+// A chunk of R <= 8 rows (a short prompt, or the tail of an expert's rows)
+// would fill a 32-row MFMA tile mostly with padding, and the product kernel
+// decodes every weight block into MFMA operands however few rows use it.
+// Here each lane owns one weight row: it reads its row's 16-byte block of the
+// tiled layout (a wave reads 1 KB contiguous per block), expands the codes to
+// int8, and takes the exact int32 dot of each 32-value block with every row of
+// the chunk by v_dot4_i32_i8 (four products per instruction).  The chunk's
+// q8_1 rows sit in LDS, read as broadcasts.  The epilogue is the product
+// kernel's, operation for operation:
+//   acc = fmaf(dx_b, dw_b * (float)dot_b, acc),  blocks b in K order,
+// so results equal the MFMA path's bit for bit ("Strata" PR #2145
+// description: exact int32 block sums; PR #3752 commit list: a per-32-value
+// fp32 epilogue in K order).  Q2_0 codes c in {0..3} enter the dot as int8
+// and the weight's -2 offset comes from the q8_1 block sum s:
+//   sum (c - 2) q = sum c q - 2 s.
+// NL4 codes index the sorted int8 codebook through two byte permutes.
+#include "internal.h"
+#include "q8_1.cuh"
+
+#include <hip/hip_runtime.h>
+
+namespace moe {
+
+namespace {
+
+constexpr int kModeOut = 0, kModeDots = 1, kModeSwiglu = 2;   // as in the product kernel
+constexpr int kSmallWaves = 4;        // 256 weight rows per workgroup, one per lane
+constexpr int kSmallSlots = 8;        // weight blocks loaded ahead
+
+struct SmallRaw {
+    uint4 c;          // the lane's 16 code bytes of one block
+    uint32_t s;       // its binary16 scale
+};
+
+__device__ __forceinline__ float half_to_float(uint32_t bits) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+}
+
+// Codes of one dword of a Q2_0 block, field j: values 16 j + 4 m .. + 3 as int8 0..3.
+template <int J>
+__device__ __forceinline__ uint32_t q2_field(uint32_t w) {
+    return (w >> (2 * J)) & 0x03030303u;
+}
+
+// NL4: four 4-bit codes (one per byte) -> four int8 codebook entries.
+__device__ __forceinline__ uint32_t nl4_lookup4(uint32_t idx, const uint32_t (&cb)[4]) {
+    const uint32_t i7 = idx & 0x07070707u;
+    const uint32_t lo = __builtin_amdgcn_perm(cb[1], cb[0], i7);      // entries 0..7
+    const uint32_t hi = __builtin_amdgcn_perm(cb[3], cb[2], i7);      // entries 8..15
+    // byte k from hi where bit 3 of its code is set: selector 4 + k, else k
+    const uint32_t sel = ((idx & 0x08080808u) >> 1) | 0x03020100u;
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+template <int WTYPE, int MODE>
+__global__ __launch_bounds__(64 * kSmallWaves) void expert_small_kernel(ProductArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t s_act[kSmallActBytes];
+
+    const int bid = blockIdx.x;
+    const int xcd = bid % kXcds;
+    const int jj = bid / kXcds;
+    const int xcnt = a.xcd_small[kXcds + xcd];
+    if (jj >= xcnt * a.n_tiles) return;
+    const int c = a.xcd_small[xcd] + jj / a.n_tiles;
+    const int tile = jj % a.n_tiles;
+    const int expert = a.chunks[4 * c + 0];
+    const int row0 = a.chunks[4 * c + 1];
+    const int nrows = a.chunks[4 * c + 2];
+    if (nrows > a.small_rows) return;                 // never: the lists hold small experts only
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int half = lane >> 5;                       // which of the wave's two 32-row tiles
+    const int col = lane & 31;
+    const int cols = a.cols;
+    constexpr int WB = WTYPE == 1 ? 64 : 32;          // values per weight block
+    const int nbw = cols / WB;
+    const int nb32 = cols >> 5;
+    const uint32_t arb = uint32_t(cols) + uint32_t(nb32) * 8u;      // q8_1 row bytes
+    const uint32_t lstride = (arb + 15u) & ~15u;                    // LDS row stride
+
+    // the wave's rows: as in the product kernel, gate/up fused takes gate rows
+    // j0..j0+31 in lanes 0..31 and the up rows of the same j's in lanes 32..63
+    const int n_ff = a.out_rows >> 1;
+    const int n0 = tile * (MODE == kModeSwiglu ? 128 : 256);
+    const int nw = MODE == kModeSwiglu ? n0 + 32 * wave : n0 + 64 * wave;
+    const bool wave_on = nw < (MODE == kModeSwiglu ? n_ff : a.out_rows);
+    const int tb = half == 0 ? nw : (MODE == kModeSwiglu ? n_ff + nw : nw + 32);
+    const int wrow = tb + col;
+    const uint32_t wr = uint32_t(min(wrow, a.out_rows - 1));
+    const uint8_t *wexp = a.w_base + a.w_off[expert];
+    const uint16_t *wscales = reinterpret_cast<const uint16_t *>(wexp + size_t(a.out_rows) * nbw * 16);
+    const uint32_t soff = (wr & ~31u) * uint32_t(nbw) + (wr & 31u);  // tiled slot of block 0
+    auto wload = [&](int blk) {
+        const int b = min(blk, nbw - 1);
+        SmallRaw r;
+        r.c = *reinterpret_cast<const uint4 *>(wexp + (size_t(b) * 32 + soff) * 16);
+        r.s = wscales[size_t(b) * 32 + soff];
+        return r;
+    };
+
+    SmallRaw slot[kSmallSlots];
+#pragma unroll
+    for (int x = 0; x < kSmallSlots; ++x) slot[x] = wload(x);
+
+    // the chunk's q8_1 rows into LDS, 8 bytes at a time (rows are 8-byte
+    // aligned): every load of the thread is issued before the first store
+    {
+        constexpr int kPer = kSmallActBytes / 8 / (64 * kSmallWaves);
+        const uint8_t *src = a.act + size_t(row0) * arb;
+        const uint32_t per_row = arb / 8u;
+        const uint32_t n = uint32_t(nrows) * per_row;
+        uint2 v[kPer];
+#pragma unroll
+        for (int x = 0; x < kPer; ++x) {
+            const uint32_t i = uint32_t(tid) + uint32_t(x) * (64 * kSmallWaves);
+            const uint32_t r = i / per_row, k = i - r * per_row;
+            if (i < n) v[x] = *reinterpret_cast<const uint2 *>(src + size_t(r) * arb + 8u * k);
+        }
+#pragma unroll
+        for (int x = 0; x < kPer; ++x) {
+            const uint32_t i = uint32_t(tid) + uint32_t(x) * (64 * kSmallWaves);
+            const uint32_t r = i / per_row, k = i - r * per_row;
+            if (i < n) *reinterpret_cast<uint2 *>(s_act + r * lstride + 8u * k) = v[x];
+        }
+    }
+    __syncthreads();
+
+    uint32_t cb[4] = {0u, 0u, 0u, 0u};
+    if constexpr (WTYPE == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            cb[i] = uint32_t(uint8_t(a.codebook[4 * i])) | (uint32_t(uint8_t(a.codebook[4 * i + 1])) << 8) |
+                    (uint32_t(uint8_t(a.codebook[4 * i + 2])) << 16) |
+                    (uint32_t(uint8_t(a.codebook[4 * i + 3])) << 24);
+    }
+
+    float acc[kMaxSmallRows];
+#pragma unroll
+    for (int i = 0; i < kMaxSmallRows; ++i) acc[i] = 0.0f;
+
+    const uint8_t *dx_base = s_act + cols;                      // fp32 d of each 32-block
+    const uint8_t *s_base = s_act + cols + 4 * nb32;            // int32 s of each 32-block
+
+    // one weight block: its int32 dots with every row, then the epilogue
+    auto block = [&](const SmallRaw &w, int blk) {
+        const float dw = half_to_float(w.s);
+        const uint32_t cw[4] = {w.c.x, w.c.y, w.c.z, w.c.w};
+        if constexpr (WTYPE == 1) {
+            // fields 0, 1 pair with q8_1 block 2 blk, fields 2, 3 with block 2 blk + 1
+            uint32_t e[4][4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                e[0][m] = q2_field<0>(cw[m]);
+                e[1][m] = q2_field<1>(cw[m]);
+                e[2][m] = q2_field<2>(cw[m]);
+                e[3][m] = q2_field<3>(cw[m]);
+            }
+#pragma unroll
+            for (int i = 0; i < kMaxSmallRows; ++i) {
+                if (i >= nrows) break;
+                const uint8_t *arow = s_act + i * lstride;
+                const uint4 *q = reinterpret_cast<const uint4 *>(arow + 64 * blk);
+                const uint4 q0 = q[0], q1 = q[1], q2 = q[2], q3 = q[3];
+                const uint32_t qv[16] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w,
+                                         q2.x, q2.y, q2.z, q2.w, q3.x, q3.y, q3.z, q3.w};
+                int d0 = 0, d1 = 0;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    d0 = __builtin_amdgcn_sdot4(int(e[0][m]), int(qv[m]), d0, false);
+                    d0 = __builtin_amdgcn_sdot4(int(e[1][m]), int(qv[4 + m]), d0, false);
+                    d1 = __builtin_amdgcn_sdot4(int(e[2][m]), int(qv[8 + m]), d1, false);
+                    d1 = __builtin_amdgcn_sdot4(int(e[3][m]), int(qv[12 + m]), d1, false);
+                }
+                const int2 sb = *reinterpret_cast<const int2 *>(s_base + i * lstride + 8 * blk);
+                const float2 dxb = *reinterpret_cast<const float2 *>(dx_base + i * lstride + 8 * blk);
+                d0 -= 2 * sb.x;
+                d1 -= 2 * sb.y;
+                if constexpr (MODE == kModeDots) {
+                    const int rr = row0 + i - a.dots_row_begin;
+                    if (wave_on && wrow < a.out_rows && rr >= 0 && rr < a.dots_n_rows) {
+                        int32_t *dst = a.dots + (size_t(rr) * a.out_rows + wrow) * nb32 + 2 * blk;
+                        dst[0] = d0;
+                        dst[1] = d1;
+                    }
+                } else {
+                    acc[i] = __builtin_fmaf(dxb.x, dw * static_cast<float>(d0), acc[i]);
+                    acc[i] = __builtin_fmaf(dxb.y, dw * static_cast<float>(d1), acc[i]);
+                }
+            }
+        } else {
+            // NL4: low nibbles of dword m are values 4 m..4 m+3, high nibbles 16 + 4 m..
+            uint32_t e[8];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                e[m] = nl4_lookup4(cw[m] & 0x0F0F0F0Fu, cb);
+                e[4 + m] = nl4_lookup4((cw[m] >> 4) & 0x0F0F0F0Fu, cb);
+            }
+#pragma unroll
+            for (int i = 0; i < kMaxSmallRows; ++i) {
+                if (i >= nrows) break;
+                const uint8_t *arow = s_act + i * lstride;
+                const uint4 *q = reinterpret_cast<const uint4 *>(arow + 32 * blk);
+                const uint4 q0 = q[0], q1 = q[1];
+                const uint32_t qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+                int d = 0;
+#pragma unroll
+                for (int m = 0; m < 8; ++m) d = __builtin_amdgcn_sdot4(int(e[m]), int(qv[m]), d, false);
+                const float dx = *reinterpret_cast<const float *>(dx_base + i * lstride + 4 * blk);
+                if constexpr (MODE == kModeDots) {
+                    const int rr = row0 + i - a.dots_row_begin;
+                    if (wave_on && wrow < a.out_rows && rr >= 0 && rr < a.dots_n_rows)
+                        a.dots[(size_t(rr) * a.out_rows + wrow) * nb32 + blk] = d;
+                } else {
+                    acc[i] = __builtin_fmaf(dx, dw * static_cast<float>(d), acc[i]);
+                }
+            }
+        }
+    };
+
+    // the block stream, kSmallSlots ahead; loads past the end are clamped
+    for (int b0 = 0; b0 < nbw; b0 += kSmallSlots) {
+#pragma unroll
+        for (int x = 0; x < kSmallSlots; ++x) {
+            const int blk = b0 + x;
+            if (blk < nbw) block(slot[x], blk);
+            slot[x] = wload(blk + kSmallSlots);
+        }
+    }
+
+    if constexpr (MODE == kModeSwiglu) {
+        if (!wave_on) return;
+        const size_t hrb = size_t(n_ff) + size_t(n_ff >> 5) * 8;
+        const int j = nw + col;                                   // the lane's j
+#pragma unroll
+        for (int i = 0; i < kMaxSmallRows; ++i) {
+            if (i >= nrows) break;
+            // lanes 0..31 hold gate, 32..63 up of the same j
+            const float g = acc[i];
+            const float u = __shfl_xor(acc[i], 32);
+            const float e = static_cast<float>(exp(-static_cast<double>(g)));
+            const float h = g / (1.0f + e) * u;
+            float amax = __builtin_fabsf(h);
+#pragma unroll
+            for (int s = 1; s < 32; s <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, s));
+            const float d = amax / 127.0f;
+            const int q = d != 0.0f ? int(q8_round(h, d)) : 0;
+            int sum = q;
+#pragma unroll
+            for (int s = 1; s < 32; s <<= 1) sum += __shfl_xor(sum, s);
+            uint8_t *hrow = a.hq + size_t(row0 + i) * hrb;
+            if (half == 0) {
+                hrow[j] = uint8_t(int8_t(q));
+                if (col == 0) {
+                    reinterpret_cast<float *>(hrow + n_ff)[j >> 5] = d;
+                    reinterpret_cast<int32_t *>(hrow + n_ff + 4 * (n_ff >> 5))[j >> 5] = sum;
+                }
+            }
+        }
+    } else if constexpr (MODE == kModeOut) {
+        if (!wave_on || wrow >= a.out_rows) return;
+#pragma unroll
+        for (int i = 0; i < kMaxSmallRows; ++i) {
+            if (i >= nrows) break;
+            const int rr = row0 + i;
+            const size_t orow = a.perm ? size_t(a.perm[rr]) : size_t(rr);
+            a.out[orow * a.out_rows + wrow] = acc[i];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_expert_small(const ProductArgs &a, hipStream_t stream) {
+    if (a.max_items <= 0 || a.small_rows <= 0) return hipSuccess;
+    const dim3 grid(kXcds * a.max_items), block(64 * kSmallWaves);
+    if (a.wtype == 1) {
+        if (a.dots)
+            hipLaunchKernelGGL((expert_small_kernel<1, kModeDots>), grid, block, 0, stream, a);
+        else if (a.hq)
+            hipLaunchKernelGGL((expert_small_kernel<1, kModeSwiglu>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((expert_small_kernel<1, kModeOut>), grid, block, 0, stream, a);
+    } else {
+        if (a.dots)
+            hipLaunchKernelGGL((expert_small_kernel<2, kModeDots>), grid, block, 0, stream, a);
+        else if (a.hq)
+            hipLaunchKernelGGL((expert_small_kernel<2, kModeSwiglu>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((expert_small_kernel<2, kModeOut>), grid, block, 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

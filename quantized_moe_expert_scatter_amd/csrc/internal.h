@@ -12,6 +12,8 @@ namespace moe {
 constexpr int kXcds = 8;           // MI355X: 8 accelerator dies, each with its own L2
 constexpr int kMaxChunkRows = 128;  // rows of one chunk = four 32-row MFMA tiles
 constexpr int kTileRows = 256;     // weight rows (outputs) per workgroup: 4 waves x 64
+constexpr int kMaxSmallRows = 8;      // chunks of at most this many rows take the small kernel
+constexpr int kSmallActBytes = 32768; // its LDS for the chunk's q8_1 rows
 constexpr uint32_t kMagicBits = 0x4B400000u;  // 1.5 * 2^23 as binary32
 
 constexpr size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
@@ -26,7 +28,7 @@ struct PlanLayout {
     size_t perm;     // int32 [R]     sorted row -> t*K+k
     size_t inv;      // int32 [R]     t*K+k -> sorted row
     size_t chunks;   // int32 [maxc][4] chunk table grouped by XCD (see xcd)
-    size_t xcd;      // int32 [2*kXcds]: first chunk and chunk count of each XCD list
+    size_t xcd;      // int32 [kXcdRows][kXcds]: the XCD lists, see XcdRow
     size_t gu_off;   // uint64 [E]    gate/up expert byte offsets
     size_t dn_off;   // uint64 [E]    down expert byte offsets
     // built on the device only (moe_prefill_plan_device); zero in a host plan
@@ -39,6 +41,20 @@ struct PlanLayout {
 // Experts a device-built plan takes (its scheduling workgroup stages four
 // int32 arrays of this length in LDS, 32 KB).
 constexpr int kPlanMaxExperts = 2048;
+
+// Rows of the XCD table (kXcds entries each).  List x is chunks
+// [start[x], start[x] + count[x]) of the XCD-grouped chunk table, experts in
+// rank order, each expert's chunks together; for product p (0 gate/up, 1
+// down) the chunks of experts with more rows than small_rows_for(that
+// product's contraction length) come first ("large", the product kernel's
+// items) and the rest follow ("small", the small kernel's).  Each view is a
+// (start, count) pair of rows, so a kernel reads xcd[x] and xcd[kXcds + x].
+enum XcdRow {
+    kXcdStart = 0, kXcdCount = 1,
+    kXcdLarge = 2,    // + 4 p: start, count of product p's large chunks
+    kXcdSmall = 4,    // + 4 p: start, count of product p's small chunks
+    kXcdRows = 10
+};
 
 // Scratch of the device-built plan, int32 indices into the aux section.
 struct PlanAux {
@@ -56,7 +72,7 @@ inline PlanLayout plan_layout(int tokens, int topk, int n_expert, int chunk_rows
     L.perm = o;   o += align16(R * 4);
     L.inv = o;    o += align16(R * 4);
     L.chunks = o; o += align16(size_t(max_chunks(int(R), n_expert, chunk_rows)) * 16);
-    L.xcd = o;    o += align16(size_t(2 * kXcds) * 4);
+    L.xcd = o;    o += align16(size_t(kXcdRows * kXcds) * 4);
     L.gu_off = o; o += align16(size_t(n_expert) * 8);
     L.dn_off = o; o += align16(size_t(n_expert) * 8);
     L.counts = o; o += align16(size_t(n_expert + 1) * 4);
@@ -72,7 +88,8 @@ struct ProductArgs {
     const uint8_t *w_base;     // weight buffer
     const uint64_t *w_off;     // device: expert byte offsets
     const int32_t *chunks;     // device: XCD-grouped chunk table
-    const int32_t *xcd;        // device: per-XCD list starts and counts
+    const int32_t *xcd;        // device: per-XCD (start, count) rows of this launch's items
+    const int32_t *xcd_small;  // device: the same for the small kernel's items
     const int32_t *perm;       // device: sorted row -> output row (NULL: identity)
     float *out;                // fp32 outputs
     uint8_t *hq;               // gate/up fused with swiglu: q8_1 rows of H (else NULL)
@@ -84,6 +101,7 @@ struct ProductArgs {
     int max_items;             // items per XCD list (grid = kXcds * max_items)
     int dots_row_begin;
     int dots_n_rows;
+    int small_rows;            // chunks of <= small_rows rows go to the small kernel (0: none)
     int8_t codebook[16];
 };
 
@@ -93,10 +111,20 @@ hipError_t launch_quantize_scatter(const float *x, int tokens, int hidden, int t
 hipError_t launch_swiglu_q8(const float *gu, int rows, int n_ff, uint8_t *hq,
                             hipStream_t stream);
 hipError_t launch_expert_product(const ProductArgs &args, hipStream_t stream);
+// The same product for the items whose chunk has at most args.small_rows rows
+// (one lane per weight row, int8 dot products); launch_expert_product skips them.
+hipError_t launch_expert_small(const ProductArgs &args, hipStream_t stream);
+// Rows a chunk may have to take the small kernel at this contraction length.
+inline int small_rows_for(int cols) {
+    const int lstride = int(align16(size_t(cols) + size_t(cols / 32) * 8));
+    const int fit = kSmallActBytes / lstride;
+    return fit < kMaxSmallRows ? fit : kMaxSmallRows;
+}
 // The plan built on the device from device routing ids (see plan_kernels.hip):
 // the perm, inv, chunk, xcd, counts, offsets and aux sections of `ws`.
 hipError_t launch_device_plan(const int32_t *ids, int rows, int n_expert, int chunk_rows,
-                              uint8_t *ws, const PlanLayout &L, hipStream_t stream);
+                              int small_gu, int small_dn, uint8_t *ws, const PlanLayout &L,
+                              hipStream_t stream);
 // out[t] = sum over k of w[t*topk+k] * dm[t*topk+k] (fmaf, k ascending);
 // the grid is tokens * ceil(hidden / 1024) workgroups of 256 threads.
 hipError_t launch_combine(const float *dm, const float *w, int tokens, int topk, int hidden,

@@ -25,9 +25,10 @@ struct moe_plan {
     std::vector<uint64_t> gu_off, dn_off;
     int8_t gu_codebook[16] = {}, dn_codebook[16] = {};
     std::vector<int32_t> counts, offsets, perm, inv, chunks, dev_chunks;
-    int32_t xcd_tab[2 * kXcds] = {};
+    int32_t xcd_tab[kXcdRows * kXcds] = {};
     int n_chunks = 0;
     int max_xcd_chunks = 0;
+    int max_large[2] = {0, 0}, max_small[2] = {0, 0};   // per product: longest list of each view
     bool device_built = false;   // sorted maps and chunk lists built on the device
     void *plan_dev = nullptr;
     PlanLayout layout{};
@@ -277,12 +278,26 @@ int moe_prefill_plan(const int32_t *ids, int tokens, int topk, int n_expert, int
             load[x] += p->counts[e];
             members[x].push_back(e);
         }
+        const int small[2] = {small_rows_for(p->hidden), small_rows_for(p->n_ff)};
         int start = 0;
         for (int x = 0; x < kXcds; ++x) {
             const std::vector<int32_t> list = chunk_list(members[x], p->counts, p->offsets, chunk_rows);
             const int cnt = int(list.size() / 4);
-            p->xcd_tab[x] = start;
-            p->xcd_tab[kXcds + x] = cnt;
+            p->xcd_tab[kXcdStart * kXcds + x] = start;
+            p->xcd_tab[kXcdCount * kXcds + x] = cnt;
+            for (int q = 0; q < 2; ++q) {
+                // members come largest first: the experts above the small
+                // kernel's row limit are a prefix of the list
+                int large = 0;
+                for (int e : members[x])
+                    if (p->counts[e] > small[q]) large += (p->counts[e] + chunk_rows - 1) / chunk_rows;
+                p->xcd_tab[(kXcdLarge + 4 * q) * kXcds + x] = start;
+                p->xcd_tab[(kXcdLarge + 4 * q + 1) * kXcds + x] = large;
+                p->xcd_tab[(kXcdSmall + 4 * q) * kXcds + x] = start + large;
+                p->xcd_tab[(kXcdSmall + 4 * q + 1) * kXcds + x] = cnt - large;
+                p->max_large[q] = std::max(p->max_large[q], large);
+                p->max_small[q] = std::max(p->max_small[q], cnt - large);
+            }
             start += cnt;
             p->max_xcd_chunks = std::max(p->max_xcd_chunks, cnt);
             p->dev_chunks.insert(p->dev_chunks.end(), list.begin(), list.end());
@@ -331,6 +346,7 @@ int moe_prefill_plan_device(const int32_t *ids_dev, int tokens, int topk, int n_
     // bound every list stays within, and the surplus workgroups exit at once
     p->n_chunks = -1;
     p->max_xcd_chunks = max_chunks(p->rows, n_expert, chunk_rows);
+    for (int q = 0; q < 2; ++q) p->max_large[q] = p->max_small[q] = p->max_xcd_chunks;
     // the two weight offset tables go up from the host, the rest is built there
     st = upload(p, L.gu_off, L.counts, stream,
                 [&](uint8_t *s) {
@@ -339,6 +355,7 @@ int moe_prefill_plan_device(const int32_t *ids_dev, int tokens, int topk, int n_
                 },
                 [&](hipStream_t hs) {
                     return launch_device_plan(ids_dev, p->rows, n_expert, chunk_rows,
+                                              small_rows_for(p->hidden), small_rows_for(p->n_ff),
                                               static_cast<uint8_t *>(plan_dev), L, hs);
                 });
     if (st) {
@@ -426,7 +443,9 @@ static ProductArgs product_args(const moe_plan *p, int product, const void *act)
     a.w_off = reinterpret_cast<const uint64_t *>(dev_at(p, product == 0 ? p->layout.gu_off
                                                                           : p->layout.dn_off));
     a.chunks = reinterpret_cast<const int32_t *>(dev_at(p, p->layout.chunks));
-    a.xcd = reinterpret_cast<const int32_t *>(dev_at(p, p->layout.xcd));
+    const int32_t *tab = reinterpret_cast<const int32_t *>(dev_at(p, p->layout.xcd));
+    a.xcd = tab + (kXcdLarge + 4 * product) * kXcds;
+    a.xcd_small = tab + (kXcdSmall + 4 * product) * kXcds;
     a.perm = product == 0 ? nullptr : reinterpret_cast<const int32_t *>(dev_at(p, p->layout.perm));
     a.wtype = base_type(w.type);
     a.cols = w.cols;
@@ -434,7 +453,20 @@ static ProductArgs product_args(const moe_plan *p, int product, const void *act)
     a.n_tiles = (w.rows + kTileRows - 1) / kTileRows;
     a.max_items = p->max_xcd_chunks * a.n_tiles;
     if (a.wtype == MOE_W_NL4) std::memcpy(a.codebook, product == 0 ? p->gu_codebook : p->dn_codebook, 16);
+    a.small_rows = small_rows_for(w.cols);
     return a;
+}
+
+// The experts of at most a.small_rows rows go to the small kernel, the others
+// to the product kernel, each over its view of the XCD lists (a.n_tiles set);
+// a launch with no item is skipped.
+static hipError_t launch_products(const moe_plan *p, int product, ProductArgs a, hipStream_t stream) {
+    hipError_t e = hipSuccess;
+    a.max_items = p->max_small[product] * a.n_tiles;
+    if (a.max_items > 0) e = launch_expert_small(a, stream);
+    a.max_items = p->max_large[product] * a.n_tiles;
+    if (e == hipSuccess && a.max_items > 0) e = launch_expert_product(a, stream);
+    return e;
 }
 
 int expert_gate_up(const moe_plan *p, const void *xq, float *gu, void *stream) {
@@ -445,7 +477,7 @@ int expert_gate_up(const moe_plan *p, const void *xq, float *gu, void *stream) {
     if (!aligned16(xq) || !aligned16(gu)) return MOE_EALIGN;
     ProductArgs a = product_args(p, 0, xq);
     a.out = gu;
-    return hip_status(launch_expert_product(a, static_cast<hipStream_t>(stream)));
+    return hip_status(launch_products(p, 0, a, static_cast<hipStream_t>(stream)));
 }
 
 int expert_gate_up_swiglu_q8(const moe_plan *p, const void *xq, void *hq, void *stream) {
@@ -457,9 +489,8 @@ int expert_gate_up_swiglu_q8(const moe_plan *p, const void *xq, void *hq, void *
     ProductArgs a = product_args(p, 0, xq);
     // work items of 128 j's: gate rows j and up rows n_ff + j together
     a.n_tiles = (p->n_ff + kTileRows / 2 - 1) / (kTileRows / 2);
-    a.max_items = p->max_xcd_chunks * a.n_tiles;
     a.hq = static_cast<uint8_t *>(hq);
-    return hip_status(launch_expert_product(a, static_cast<hipStream_t>(stream)));
+    return hip_status(launch_products(p, 0, a, static_cast<hipStream_t>(stream)));
 }
 
 int swiglu_q8(const moe_plan *p, const float *gu, void *hq, void *stream) {
@@ -480,7 +511,7 @@ int expert_down(const moe_plan *p, const void *hq, float *dm, void *stream) {
     if (!aligned16(hq) || !aligned16(dm)) return MOE_EALIGN;
     ProductArgs a = product_args(p, 1, hq);
     a.out = dm;
-    return hip_status(launch_expert_product(a, static_cast<hipStream_t>(stream)));
+    return hip_status(launch_products(p, 1, a, static_cast<hipStream_t>(stream)));
 }
 
 int moe_combine(const moe_plan *p, const float *dm, const float *w, float *out, void *stream) {
@@ -508,7 +539,7 @@ int moe_debug_block_dots(const moe_plan *p, int product, const void *act, int ro
     a.dots = dots;
     a.dots_row_begin = row_begin;
     a.dots_n_rows = n_rows;
-    return hip_status(launch_expert_product(a, static_cast<hipStream_t>(stream)));
+    return hip_status(launch_products(p, product, a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -72,6 +72,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(const int32_t 
 // in rank order beforehand, and the results go back to memory in parallel.
 __global__ __launch_bounds__(kPlanThreads) void plan_schedule_kernel(const int32_t *counts,
                                                                      int n_expert, int chunk_rows,
+                                                                     int small_gu, int small_dn,
                                                                      int32_t *offsets, int32_t *aux,
                                                                      int32_t *xcd_tab) {
     __shared__ int32_t s_counts[kPlanMaxExperts + 1];
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_schedule_kernel(const int32
     __shared__ int32_t s_rows[kPlanMaxExperts];     // rows of the expert of rank r, then its XCD
     __shared__ int32_t s_base[kPlanMaxExperts];     // its first slot in that XCD's list
     __shared__ int32_t s_wave[kPlanThreads / 64];
-    __shared__ int32_t s_listed[kXcds];
+    __shared__ int32_t s_listed[3][kXcds];     // chunks, and the large ones of each product
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_schedule_kernel(const int32
         // takes the first XCD of least rows as the least (rows << 3 | x) key
         // of lanes 0..7, by three DPP shifts of a prefix minimum
         uint32_t load = lane < kXcds ? 0u : 0x1FFFFFFFu;
-        int32_t listed = 0;
+        int32_t listed = 0, large_gu = 0, large_dn = 0;
         for (int r0 = 0; r0 < n_expert; r0 += 64) {
             const int n = min(64, n_expert - r0);
             const int32_t cvec = lane < n ? s_rows[r0 + lane] : 0;
@@ -156,6 +157,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_schedule_kernel(const int32
                 const bool mine = lane == x;            // no branch: both adds run
                 load += mine ? uint32_t(c) : 0u;
                 listed += mine ? nch : 0;
+                large_gu += mine && c > small_gu ? nch : 0;
+                large_dn += mine && c > small_dn ? nch : 0;
                 xs = lane == j ? x : xs;
                 bases = lane == j ? base : bases;
             }
@@ -164,7 +167,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_schedule_kernel(const int32
                 s_base[r0 + lane] = cvec == 0 ? 0 : bases;
             }
         }
-        if (lane < kXcds) s_listed[lane] = listed;
+        if (lane < kXcds) {
+            s_listed[0][lane] = listed;
+            s_listed[1][lane] = large_gu;
+            s_listed[2][lane] = large_dn;
+        }
     }
     __syncthreads();
     for (int r = tid; r < n_expert; r += kPlanThreads) {
@@ -176,9 +183,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_schedule_kernel(const int32
     if (tid == 0) {
         int32_t start = 0;
         for (int x = 0; x < kXcds; ++x) {
-            xcd_tab[x] = start;
-            xcd_tab[kXcds + x] = s_listed[x];
-            start += s_listed[x];
+            const int32_t cnt = s_listed[0][x];
+            xcd_tab[kXcdStart * kXcds + x] = start;
+            xcd_tab[kXcdCount * kXcds + x] = cnt;
+            for (int q = 0; q < 2; ++q) {
+                const int32_t large = s_listed[1 + q][x];
+                xcd_tab[(kXcdLarge + 4 * q) * kXcds + x] = start;
+                xcd_tab[(kXcdLarge + 4 * q + 1) * kXcds + x] = large;
+                xcd_tab[(kXcdSmall + 4 * q) * kXcds + x] = start + large;
+                xcd_tab[(kXcdSmall + 4 * q + 1) * kXcds + x] = cnt - large;
+            }
+            start += cnt;
         }
     }
 }
@@ -280,7 +295,8 @@ unsigned blocks_for(long long n) { return unsigned((n + kPlanThreads - 1) / kPla
 }  // namespace
 
 hipError_t launch_device_plan(const int32_t *ids, int rows, int n_expert, int chunk_rows,
-                              uint8_t *ws, const PlanLayout &L, hipStream_t stream) {
+                              int small_gu, int small_dn, uint8_t *ws, const PlanLayout &L,
+                              hipStream_t stream) {
     auto at = [&](size_t off) { return reinterpret_cast<int32_t *>(ws + off); };
     int32_t *perm = at(L.perm), *inv = at(L.inv), *chunks = at(L.chunks), *xcd = at(L.xcd);
     int32_t *counts = at(L.counts), *offsets = at(L.offsets), *aux = at(L.aux);
@@ -293,7 +309,7 @@ hipError_t launch_device_plan(const int32_t *ids, int rows, int n_expert, int ch
         hipLaunchKernelGGL(plan_count_kernel, dim3(blocks_for((rows + 7) / 8)), dim3(kPlanThreads), 0,
                            stream, ids, rows, n_expert, counts);
     hipLaunchKernelGGL(plan_schedule_kernel, dim3(1), dim3(kPlanThreads), 0, stream, counts, n_expert,
-                       chunk_rows, offsets, aux, xcd);
+                       chunk_rows, small_gu, small_dn, offsets, aux, xcd);
     if (rows > 0)
         hipLaunchKernelGGL(plan_scatter_kernel, dim3(n_expert + 1), dim3(kPlanThreads), 0, stream, ids,
                            rows, n_expert, counts, offsets, perm, inv);
