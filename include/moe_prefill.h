@@ -202,7 +202,10 @@ int moe_prefill_plan_device(const int32_t *ids_dev, int tokens, int topk, int n_
 int moe_plan_query(const moe_plan *plan, int *rows, int *n_chunks,
                    int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *chunks);
 
-/* Release the plan (waits for its upload to finish; does not free plan_dev). */
+/* Release the plan (waits for its upload to finish; does not free plan_dev).
+ * The pinned host buffer its upload was staged in is kept by the library for
+ * later plans (until the process ends), so destroying a plan never waits for
+ * the rest of the device. */
 void moe_plan_destroy(moe_plan *plan);
 
 /* Step 1 ("Strata" PR #3752, commit list: quantize_scatter).  Quantize each

@@ -35,12 +35,28 @@ struct PlanLayout {
     size_t counts;   // int32 [E+1]   rows per expert, then ids out of range
     size_t offsets;  // int32 [E+2]   exclusive prefix of counts
     size_t aux;      // int32 [kPlanAux(E)]: see PlanAux
+    size_t tiles;    // int32 [E+1][n_tiles]: per id tile, rows of each bucket, then
+                     // (after the scan) the bucket's rows in earlier tiles
     size_t total;
 };
 
 // Experts a device-built plan takes (its scheduling workgroup stages four
-// int32 arrays of this length in LDS, 32 KB).
+// int32 arrays of this length in LDS, 40 KB).
 constexpr int kPlanMaxExperts = 2048;
+// The device plan splits the routing ids into tiles of a multiple of 2048
+// consecutive ids (one workgroup each, 8 ids per thread and pass), at most
+// kPlanMaxTiles of them.
+constexpr int kPlanPassIds = 2048;
+constexpr int kPlanMaxTiles = 256;
+inline int plan_tile_ids(long long rows) {
+    const long long per = (rows + kPlanMaxTiles - 1) / kPlanMaxTiles;
+    const long long t = (per + kPlanPassIds - 1) / kPlanPassIds * kPlanPassIds;
+    return int(t > kPlanPassIds ? t : kPlanPassIds);
+}
+inline int plan_n_tiles(long long rows) {
+    const long long t = plan_tile_ids(rows);
+    return rows > 0 ? int((rows + t - 1) / t) : 1;
+}
 
 // Rows of the XCD table (kXcds entries each).  List x is chunks
 // [start[x], start[x] + count[x]) of the XCD-grouped chunk table, experts in
@@ -78,6 +94,7 @@ inline PlanLayout plan_layout(int tokens, int topk, int n_expert, int chunk_rows
     L.counts = o; o += align16(size_t(n_expert + 1) * 4);
     L.offsets = o; o += align16(size_t(n_expert + 2) * 4);
     L.aux = o;    o += align16(size_t(PlanAux::size(n_expert)) * 4);
+    L.tiles = o;  o += align16(size_t(n_expert + 1) * size_t(plan_n_tiles((long long)R)) * 4);
     L.total = o;
     return L;
 }

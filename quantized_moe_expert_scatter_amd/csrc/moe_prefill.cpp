@@ -13,6 +13,7 @@
 
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -32,7 +33,8 @@ struct moe_plan {
     bool device_built = false;   // sorted maps and chunk lists built on the device
     void *plan_dev = nullptr;
     PlanLayout layout{};
-    void *staging = nullptr;
+    void *staging = nullptr;     // pinned, from the staging pool
+    size_t staging_cap = 0;
     hipEvent_t uploaded = nullptr;
 };
 
@@ -133,15 +135,58 @@ std::vector<int32_t> chunk_list(const std::vector<int> &order, const std::vector
     return chunks;
 }
 
+// Pinned host buffers for the plans' uploads, kept for reuse until the
+// process ends: hipHostMalloc costs tens of microseconds per plan and
+// hipHostFree waits for the whole device, which would stall a caller that
+// destroys one layer's plan while later layers run.  A plan takes the
+// smallest free buffer that fits, or a new one of the next power of two, and
+// gives it back when destroyed, once its copy has completed.
+class StagingPool {
+  public:
+    void *take(size_t n, size_t *cap) {
+        {
+            std::lock_guard<std::mutex> g(m_);
+            size_t best = free_.size();
+            for (size_t i = 0; i < free_.size(); ++i)
+                if (free_[i].first >= n && (best == free_.size() || free_[i].first < free_[best].first))
+                    best = i;
+            if (best < free_.size()) {
+                void *ptr = free_[best].second;
+                *cap = free_[best].first;
+                free_.erase(free_.begin() + long(best));
+                return ptr;
+            }
+        }
+        size_t c = 4096;
+        while (c < n) c <<= 1;
+        void *ptr = nullptr;
+        // portable: a buffer may serve a plan on another device later
+        if (hipHostMalloc(&ptr, c, hipHostMallocPortable) != hipSuccess) return nullptr;
+        *cap = c;
+        return ptr;
+    }
+    void give(void *ptr, size_t cap) {
+        std::lock_guard<std::mutex> g(m_);
+        free_.emplace_back(cap, ptr);
+    }
+
+  private:
+    std::mutex m_;
+    std::vector<std::pair<size_t, void *>> free_;
+};
+
+StagingPool &staging_pool() {
+    static StagingPool *pool = new StagingPool;     // never destroyed: outlives every plan
+    return *pool;
+}
+
 // Pinned staging of workspace bytes [begin, end), copied up asynchronously on
 // `stream`; p->uploaded is recorded after `then` (further work on the stream).
 template <class Fill, class Then>
 int upload(moe_plan *p, size_t begin, size_t end, void *stream, Fill fill, Then then) {
     const size_t n = end - begin;
-    if (hipHostMalloc(&p->staging, n > 0 ? n : 16, hipHostMallocDefault) != hipSuccess) {
-        p->staging = nullptr;
-        return MOE_EHIP;
-    }
+    p->staging = staging_pool().take(n > 0 ? n : 16, &p->staging_cap);
+    if (!p->staging) return MOE_EHIP;
     uint8_t *s = static_cast<uint8_t *>(p->staging);
     std::memset(s, 0, n);
     fill(s - begin);                      // fill writes at workspace offsets
@@ -153,8 +198,14 @@ int upload(moe_plan *p, size_t begin, size_t end, void *stream, Fill fill, Then 
     if (n > 0 && hipMemcpyAsync(static_cast<uint8_t *>(p->plan_dev) + begin, s, n,
                                 hipMemcpyHostToDevice, hs) != hipSuccess)
         return MOE_EHIP;
-    if (then(hs) != hipSuccess || hipEventRecord(p->uploaded, hs) != hipSuccess) return MOE_EHIP;
-    return MOE_OK;
+    // the event follows the copy whatever `then` returns: destroying the plan
+    // waits for it before the staging buffer is reused
+    const hipError_t launched = then(hs);
+    if (hipEventRecord(p->uploaded, hs) != hipSuccess) {
+        (void)hipStreamSynchronize(hs);
+        return MOE_EHIP;
+    }
+    return launched == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
 }  // namespace
@@ -306,7 +357,8 @@ int moe_prefill_plan(const int32_t *ids, int tokens, int topk, int n_expert, int
 
     if (plan_dev) {
         p->plan_dev = plan_dev;
-        st = upload(p, 0, L.total, stream,
+        // the sections after dn_off are the device-built plan's own
+        st = upload(p, 0, L.counts, stream,
                     [&](uint8_t *s) {
                         std::memcpy(s + L.perm, p->perm.data(), size_t(R) * 4);
                         std::memcpy(s + L.inv, p->inv.data(), size_t(R) * 4);
@@ -410,7 +462,8 @@ void moe_plan_destroy(moe_plan *p) {
         (void)hipEventSynchronize(p->uploaded);
         (void)hipEventDestroy(p->uploaded);
     }
-    if (p->staging) (void)hipHostFree(p->staging);
+    // the copy from the staging buffer has completed (or never started)
+    if (p->staging) staging_pool().give(p->staging, p->staging_cap);
     delete p;
 }
 

@@ -25,10 +25,18 @@ def _a16(n):
     return (n + 15) & ~15
 
 
-def _device_only_bytes(E):
+def _n_tiles(R):
+    """Id tiles of the device plan: multiples of 2048 ids, at most 256 tiles."""
+    per = -(-R // 256)
+    tile = max(2048, -(-per // 2048) * 2048)
+    return -(-R // tile) if R > 0 else 1
+
+
+def _device_only_bytes(E, R):
     """Bytes of the sections only a device-built plan fills (counts, offsets,
-    scratch), which sit at the end of the workspace."""
-    return _a16(4 * (E + 1)) + _a16(4 * (E + 2)) + _a16(4 * (3 * E + 4))
+    scratch, per-tile bucket counts), which sit at the end of the workspace."""
+    return (_a16(4 * (E + 1)) + _a16(4 * (E + 2)) + _a16(4 * (3 * E + 4))
+            + _a16(4 * (E + 1) * _n_tiles(R)))
 
 
 def _weights(E, H=128, F=64):
@@ -51,14 +59,15 @@ def _both_plans(ids, E, C):
                                if ids.size else np.zeros(4, np.int32)).cuda()
     pd = _lib.moe_prefill_plan_device(ids_dev, T, K, E, C, w_gu, w_dn, ws_d)
     torch.cuda.synchronize()
-    return ph, pd, ws_h, ws_d, n - _device_only_bytes(E)
+    return ph, pd, ws_h, ws_d, n - _device_only_bytes(E, T * K)
 
 
 CASES = [
     ("uniform", 300, 16, 4, 8), ("lognormal", 500, 32, 6, 16), ("uniform", 64, 8, 2, 64),
     ("lognormal", 2048, 512, 10, 64), ("flat", 768, 512, 10, 128), ("lognormal", 4096, 512, 10, 128),
     ("uniform", 1, 8, 2, 1), ("uniform", 130, 2, 1, 37), ("empty", 0, 8, 2, 64),
-    ("uniform", 16384, 512, 10, 128),
+    ("uniform", 16384, 512, 10, 128), ("lognormal", 3001, 2048, 7, 32),
+    ("uniform", 60000, 64, 10, 128),
 ]
 
 
@@ -82,10 +91,12 @@ def test_device_plan_bytes_equal_host_plan(kind, T, E, K, C):
 
 
 def test_device_plan_runs_the_same_chain():
-    """The lognormal small layer and the 2K layer, host plan vs device plan,
-    every output byte."""
+    """Host plan vs device plan, every output byte: the lognormal small layer,
+    the 2K layer, the 128-token layer (its down product's small-chunk items
+    outnumber the workgroups a device plan launches per XCD, so they take
+    several each) and the 16K layer (the same for the product kernel)."""
     for cfg in (wl.small_config("lognormal", 400, 256, 128, 32, 6, routing_kind="lognormal", seed=23),
-                wl.CONFIGS["2k"]):
+                wl.CONFIGS["2k"], wl.CONFIGS["t128"], wl.CONFIGS["16k"]):
         print("case", cfg.name, flush=True)
         L = wl.make_layer(cfg)
         outs = []
