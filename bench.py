@@ -30,9 +30,10 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 # the products run on fp16 matrix cores (int8 values and 2/4-bit weights are
 # exact in fp16): dense fp16 MFMA peak
 MFMA_F16_PEAK_TFLOPS = 2500.0
-# fp32 FMA on the vector ALU: 256 CU x 4 SIMD x 32 lanes per clock x 2 flop x
-# 2.4 GHz = 157.3 TFLOP/s.  A wave64 v_fmac_f32 on VGPR operands issues every
-# ~2.3 clocks on gfx950 (measured), so this rate needs no packed instructions.
+# fp32 FMA on the vector ALU, MI355X's published rate: 256 CU x 4 SIMD x 32
+# lanes per clock x 2 flop x 2.4 GHz = 157.3 TFLOP/s.  That rate counts the
+# packed two-wide fp32 forms, which these kernels do not use: a plain wave64
+# v_fmac_f32 holds its SIMD for 4 cycles (measured), half of it.
 VALU_F32_PEAK_TFLOPS = 256 * 4 * 32 * 2 * 2.4e9 / 1e12
 # the timed step: the whole path in three launches (gate/up, swiglu and q8_1
 # fused); the four-launch form with GU in memory is reported alongside
@@ -151,6 +152,19 @@ def traffic_for(kernel, workload):
     return rec.get("bytes_per_launch")
 
 
+def issue_for(kernel, workload):
+    """VALU and MFMA busy fractions of a kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"issue_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb").read()
+    if rec.get("source_sha1") != hashlib.sha1(src).hexdigest():
+        return None
+    return {k: rec[k] for k in ("valu_busy", "mfma_busy", "cycles_per_valu_instruction", "clock_ghz")}
+
+
 def run_cpu_baseline(L, threads, target_rows):
     from oracle import oracle
     cfg = L.cfg
@@ -219,7 +233,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the clock needs tens of ms of load to settle after the host-side input
+    # generation between layers: 5 warm-up steps read 0.63 ms at 2,048 tokens
+    # against 0.56 in steady state
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="16k",
                     help="tiny | 2k | 8k | 16k | t128, or a sweep layer sw<T>_<ln0.5|ln1.0|flat32>")
     ap.add_argument("--also", default="2k,8k,t128", help="other layers reported alongside")
@@ -298,6 +315,9 @@ def main():
     roof = {"kernel": dom, "bound": bound, "achieved": round(ach, 1), "peak": round(peak, 1),
             "unit": unit, "frac": round(ach / peak, 3),
             "traffic": traffic_for(dom, args.workload),
+            # what the counters say binds it: the share of SIMD cycles its VALU
+            # and its matrix cores are busy (rocprofv3, committed summary)
+            "issue": issue_for(dom, args.workload),
             "algorithmic_bytes_per_launch": int(main_by[dom]),
             "other_bounds": {k: {"achieved": round(v[0], 1), "peak": round(v[1], 1), "unit": v[2],
                                  "frac": round(v[0] / v[1], 3)} for k, v in fr.items() if k != bound}}

@@ -32,9 +32,10 @@
 //    oracle's.  NL4 codebook entries are exact in fp16 too; there the MFMA
 //    returns the dot itself and the epilogue is fmaf(dx, d * dot, acc) with
 //    the product rounded once, as the oracle rounds it.
-//    (On gfx950 an MFMA holds the vector ALU for a large part of its run, so
-//    the 32x32 shape, with four times the results per instruction of the
-//    16x16 one, leaves more ALU time to the epilogue.)
+//    (The kernel is bound by VALU issue -- the epilogue FMAs and the weight
+//    decode, four cycles per wave64 instruction -- with the MFMAs largely
+//    hidden under that stream; a 16x16x32 form with the same VALU count per
+//    stage measured the same.)
 //  * MFMA operands: A = weights (lane l: weight row l%32), B = activations
 //    (lane l: activation row l%32); lane half kq = l/32 holds values
 //    16g + 8kq + p (p < 8) of a 32-value block in the MFMA of half g.  Any
