@@ -167,7 +167,11 @@ __global__ __launch_bounds__(64 * kSmallWaves) void expert_small_kernel(ProductA
                 const uint4 q0 = q[0], q1 = q[1], q2 = q[2], q3 = q[3];
                 const uint32_t qv[16] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w,
                                          q2.x, q2.y, q2.z, q2.w, q3.x, q3.y, q3.z, q3.w};
-                int d0 = 0, d1 = 0;
+                // each dot starts from the -2 s of its block, so the chain of
+                // four-wide dots ends at sum (c - 2) q (integer, exact)
+                const int2 sb = *reinterpret_cast<const int2 *>(s_base + i * lstride + 8 * blk);
+                const float2 dxb = *reinterpret_cast<const float2 *>(dx_base + i * lstride + 8 * blk);
+                int d0 = -2 * sb.x, d1 = -2 * sb.y;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     d0 = __builtin_amdgcn_sdot4(int(e[0][m]), int(qv[m]), d0, false);
@@ -175,10 +179,6 @@ __global__ __launch_bounds__(64 * kSmallWaves) void expert_small_kernel(ProductA
                     d1 = __builtin_amdgcn_sdot4(int(e[2][m]), int(qv[8 + m]), d1, false);
                     d1 = __builtin_amdgcn_sdot4(int(e[3][m]), int(qv[12 + m]), d1, false);
                 }
-                const int2 sb = *reinterpret_cast<const int2 *>(s_base + i * lstride + 8 * blk);
-                const float2 dxb = *reinterpret_cast<const float2 *>(dx_base + i * lstride + 8 * blk);
-                d0 -= 2 * sb.x;
-                d1 -= 2 * sb.y;
                 if constexpr (MODE == kModeDots) {
                     const int rr = row0 + i - a.dots_row_begin;
                     if (wave_on && wrow < a.out_rows && rr >= 0 && rr < a.dots_n_rows) {

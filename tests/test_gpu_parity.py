@@ -40,6 +40,10 @@ SMALL = {
     "nl4_gu": wl.small_config("nl4_gu", 150, 448, 192, 6, 4, gu_type=wl.NL4, seed=26),
     "nl4_both": wl.small_config("nl4_both", 400, 512, 224, 6, 3, gu_type=wl.NL4,
                                 down_type=wl.NL4, seed=27),
+    # degenerate routings: one expert takes every row (full chunks and a ragged
+    # tail of one expert), and every token names every expert (top-k = E)
+    "one_expert": wl.small_config("one_expert", 300, 256, 128, 1, 1, seed=28),
+    "all_experts": wl.small_config("all_experts", 70, 256, 192, 4, 4, seed=29),
 }
 
 
