@@ -4,6 +4,8 @@ forced before any HIP call."""
 import ctypes
 import os
 import re
+import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -248,3 +250,22 @@ def test_device_plan_validation_errors():
     assert st(gu=u_gu) == -3
     assert L.moe_prefill_plan_device(DEV_IDS, 8, 2, 4, 64, ctypes.byref(w_gu.struct),
                                      ctypes.byref(w_dn.struct), FAKE_BASE, need, None, None) == -1
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """Without libmoe_prefill.so every entry point raises ImportError: there is
+    no fallback of any kind (in a child process, so this process keeps the
+    library it has loaded)."""
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import quantized_moe_expert_scatter_amd._lib as L\n"
+        "L.LIB_PATH = %r\n"
+        "try:\n"
+        "    L.moe_q8_1_bytes(4, 64)\n"
+        "except ImportError as e:\n"
+        "    print('ImportError', e)\n"
+        "    sys.exit(0)\n"
+        "sys.exit(3)\n" % (ROOT, str(tmp_path / "absent.so")))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "is missing" in r.stdout
