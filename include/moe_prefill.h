@@ -181,9 +181,11 @@ int moe_prefill_plan(const int32_t *ids_host, int tokens, int topk, int n_expert
  *              as a host-built plan of the same ids.
  *   n_expert   at most 2048, and tokens*topk below 2^29 (MOE_EINVAL beyond).
  * Nothing is read back: the call enqueues a host-to-device copy of the two
- * weight offset tables and five small integer kernels (clear; count; prefix,
- * expert ranking and XCD dealing in one workgroup; a stable ballot compaction
- * per expert; the chunk lists), then returns.  An id outside [0, n_expert)
+ * weight offset tables and four small integer launches (per tile of ids, its
+ * rows per expert, which also clears the chunk table; per expert, a prefix
+ * over the tiles; one launch whose first workgroup takes the offsets, ranks
+ * the experts and deals them to the XCDs while the others place each tile's
+ * rows, stable in t*topk+k order; the chunk lists), then returns.  An id outside [0, n_expert)
  * cannot be refused at the call: its rows join no product (their outputs are
  * left unwritten) and moe_plan_query on the plan returns MOE_EINVAL.  Because
  * the per-XCD chunk counts stay on the device, the product launches over such
