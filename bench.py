@@ -26,6 +26,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "ms/layer + effective int8 TOPS (512 experts, top-10) at 2K/8K/16K tokens"
+# "Strata" PR #2145, Kernels table: the fused int8 expert layer on an RTX 2080
+# Ti at 2,048 and 16,384 tokens (ms per layer)
+PAGES_MS = {"2k": 6.61, "16k": 37.15}
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 # the products run on fp16 matrix cores (int8 values and 2/4-bit weights are
 # exact in fp16): dense fp16 MFMA peak
@@ -353,6 +356,11 @@ def main():
                    for k, v in results.items()},
         "roofline": roof,
         "cpu_baseline": cpu,
+        # the pages' own figures for one layer (512 experts, top 10), measured on
+        # an RTX 2080 Ti with real model weights: context, not a target
+        "context": {"pages_ms_per_layer_rtx2080ti": PAGES_MS,
+                    "ratio_to_pages": {k: round(PAGES_MS[k] / results[k]["ms_per_layer"], 2)
+                                       for k in PAGES_MS if k in results}},
     }
     print(json.dumps(line), flush=True)
 
