@@ -46,9 +46,12 @@
 //    8q + 4kq + i (q, i < 4), stored as four float4.
 //  * Raw weight and activation bytes are loaded 2-6 stages ahead of their use
 //    (deeper when the chunk has fewer rows and registers allow); every load
-//    is unconditional from a clamped, in-bounds address, so no in-flight
-//    register is copied (a copy would make the compiler wait for every
-//    outstanding load).
+//    is unconditional, so no in-flight register is copied (a copy would make
+//    the compiler wait for every outstanding load).  Loads go through buffer
+//    descriptors (one per expert's weights, one per chunk's rows): a lane's
+//    offset stays in a register, the stage's offset is a scalar, so the
+//    loop computes no 64-bit addresses, and the descriptor's range check
+//    keeps every access inside the expert or the chunk.
 //  * Work lists are grouped per XCD (workgroup id i runs on XCD i % 8): all
 //    chunks of an expert land on one XCD, so its weight tiles and activation
 //    rows are re-read from that XCD's L2.
@@ -145,28 +148,6 @@ struct ARaw {
     uint4 q0, q1;
     float d;
 };
-
-// codes/scales: the expert's planes advanced to the stage (wave-uniform);
-// coff/soff: the lane's byte offset of its code bytes and element offset of
-// its scale within them (32-bit, so the loads take a scalar base).
-template <int WTYPE>
-__device__ __forceinline__ WRaw load_weights(const uint8_t *codes, const uint16_t *scales, uint32_t coff,
-                                             uint32_t soff, bool second) {
-    WRaw w;
-    if constexpr (WTYPE == 1) {
-        w.c0 = *reinterpret_cast<const uint2 *>(codes + coff);
-        w.c1 = w.c0;
-        w.s = scales[soff];
-    } else {
-        // the second block of a half-filled last stage is clamped to the first
-        // the next block of the same 32 rows is 32 slots further
-        const uint32_t o1 = second ? 32u : 0u;
-        w.c0 = *reinterpret_cast<const uint2 *>(codes + coff);
-        w.c1 = *reinterpret_cast<const uint2 *>(codes + coff + 16u * o1);
-        w.s = uint32_t(scales[soff]) | (uint32_t(scales[soff + o1]) << 16);
-    }
-    return w;
-}
 
 // The 8 fp16 weights lane half kq feeds to MFMA g of 32-value block h of the
 // stage: values 16g + 8kq + p of the block.  Q2_0 (block h is half h of the
@@ -366,7 +347,6 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
     // weights (tiled layout: block b of row 32i + r at slot (i * nbw + b) * 32 + r):
     // this lane's row in each of the wave's two tiles (clamped for loads)
     const uint8_t *wexp = a.w_base + a.w_off[expert];
-    const uint16_t *wscales = reinterpret_cast<const uint16_t *>(wexp + size_t(a.out_rows) * nbw * 16);
     const int n_ff = a.out_rows >> 1;
     const int nw = MODE == kSwiglu ? n0 + 32 * wave : n0 + 64 * wave;
     const bool wave_on = nw < (MODE == kSwiglu ? n_ff : a.out_rows);
@@ -387,11 +367,29 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
                     (uint32_t(uint8_t(a.codebook[4 * i + 2])) << 16) |
                     (uint32_t(uint8_t(a.codebook[4 * i + 3])) << 24);
     }
+    // the expert's two planes through one buffer descriptor: the lane's
+    // offsets stay in registers, the stage's offset goes in a scalar
+    const uint32_t codes_bytes = uint32_t(a.out_rows) * uint32_t(nbw) * 16u;
+    const __amdgpu_buffer_rsrc_t wres =
+        __builtin_amdgcn_make_buffer_rsrc((void *)wexp, 0, int(codes_bytes + codes_bytes / 8u), 0x00020000);
     auto wload = [&](int stage, int t) {
         const int s = min(stage, n_stages - 1);
         const int blk = s * (kKS / WB);                      // first block of the stage
         const bool second = WTYPE == 2 && blk + 1 < nbw;
-        return load_weights<WTYPE>(wexp + size_t(blk) * 512, wscales + 32 * blk, coff[t], soff[t], second);
+        WRaw w;
+        const int cs = blk * 512, ss = int(codes_bytes) + blk * 64;
+        if constexpr (WTYPE == 1) {
+            w.c0 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(wres, coff[t], cs, 0));
+            w.c1 = w.c0;
+            w.s = __builtin_amdgcn_raw_buffer_load_b16(wres, 2u * soff[t], ss, 0);
+        } else {
+            const int o1 = second ? 32 : 0;
+            w.c0 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(wres, coff[t], cs, 0));
+            w.c1 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(wres, coff[t], cs + 16 * o1, 0));
+            w.s = uint32_t(__builtin_amdgcn_raw_buffer_load_b16(wres, 2u * soff[t], ss, 0)) |
+                  (uint32_t(__builtin_amdgcn_raw_buffer_load_b16(wres, 2u * soff[t], ss + 2 * o1, 0)) << 16);
+        }
+        return w;
     };
 
     // activations: thread tid stages row tid/2 (clamped), block tid&1 of a stage
@@ -399,12 +397,18 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
     const int sblk = tid & 1;
     const uint8_t *abase = a.act + size_t(row0) * arb;
     const uint32_t aoff = uint32_t(min(srow, nrows - 1)) * arb;
+    // the chunk's rows through one descriptor; a block past a row's last one
+    // (a half-filled last stage) reads bytes that are never used, and past the
+    // chunk the descriptor's range check returns zeros
+    const __amdgpu_buffer_rsrc_t ares =
+        __builtin_amdgcn_make_buffer_rsrc((void *)abase, 0, int(uint32_t(nrows) * arb), 0x00020000);
+    const uint32_t aq = aoff + 32u * uint32_t(sblk), ad = aoff + uint32_t(cols) + 4u * uint32_t(sblk);
     auto aload = [&](int stage) {
-        const int kb = min(min(stage, n_stages - 1) * 2 + sblk, nb32 - 1);
+        const int s = min(stage, n_stages - 1);
         ARaw r;
-        r.q0 = *reinterpret_cast<const uint4 *>(abase + aoff + 32u * kb);
-        r.q1 = *reinterpret_cast<const uint4 *>(abase + aoff + 32u * kb + 16u);
-        r.d = *reinterpret_cast<const float *>(abase + aoff + uint32_t(cols) + 4u * kb);
+        r.q0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, aq, 64 * s, 0));
+        r.q1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, aq + 16u, 64 * s, 0));
+        r.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ares, ad, 8 * s, 0));
         return r;
     };
 
