@@ -92,13 +92,17 @@ __global__ __launch_bounds__(64 * kSmallWaves) void expert_small_kernel(ProductA
     const int wrow = tb + col;
     const uint32_t wr = uint32_t(min(wrow, a.out_rows - 1));
     const uint8_t *wexp = a.w_base + a.w_off[expert];
-    const uint16_t *wscales = reinterpret_cast<const uint16_t *>(wexp + size_t(a.out_rows) * nbw * 16);
+    // the expert's codes and scales planes through one buffer descriptor: the
+    // lane's offsets stay in registers, the block's offset is a scalar
+    const uint32_t codes_bytes = uint32_t(a.out_rows) * uint32_t(nbw) * 16u;
+    const __amdgpu_buffer_rsrc_t wres =
+        __builtin_amdgcn_make_buffer_rsrc((void *)wexp, 0, int(codes_bytes + codes_bytes / 8u), 0x00020000);
     const uint32_t soff = (wr & ~31u) * uint32_t(nbw) + (wr & 31u);  // tiled slot of block 0
     auto wload = [&](int blk) {
         const int b = min(blk, nbw - 1);
         SmallRaw r;
-        r.c = *reinterpret_cast<const uint4 *>(wexp + (size_t(b) * 32 + soff) * 16);
-        r.s = wscales[size_t(b) * 32 + soff];
+        r.c = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, soff * 16u, b * 512, 0));
+        r.s = __builtin_amdgcn_raw_buffer_load_b16(wres, soff * 2u, int(codes_bytes) + b * 64, 0);
         return r;
     };
 
