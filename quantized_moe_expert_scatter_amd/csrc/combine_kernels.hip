@@ -19,8 +19,8 @@ namespace moe {
 
 namespace {
 
-constexpr int kCombineThreads = 256;   // one float4 of one token per thread
-constexpr int kCombineBatch = 8;       // slots whose loads are issued together
+constexpr int kCombineThreads = 256;   // one float4 of one token per thread, over the flat range
+constexpr int kCombineBatch = 16;      // slots whose loads are issued together (all of top-10)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -33,10 +33,12 @@ __device__ __forceinline__ f32x4 load4(const f32x4 *p) {
 template <bool STREAM>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float *dm, const float *w,
                                                                   float *out, int topk, int h4,
-                                                                  int blocks_per_token) {
-    const int t = blockIdx.x / blocks_per_token;
-    const int c = (blockIdx.x - t * blocks_per_token) * kCombineThreads + threadIdx.x;
-    if (c >= h4) return;
+                                                                  long long n4) {
+    // one float4 of one token per thread over the flat (token, float4) range
+    const long long g = (long long)blockIdx.x * kCombineThreads + threadIdx.x;
+    if (g >= n4) return;
+    const int t = int(g / h4);
+    const int c = int(g - (long long)t * h4);
     const f32x4 *src = reinterpret_cast<const f32x4 *>(dm) + size_t(t) * topk * h4 + c;
     const float *wt = w + size_t(t) * topk;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -69,13 +71,13 @@ hipError_t launch_combine(const float *dm, const float *w, int tokens, int topk,
                           float *out, hipStream_t stream) {
     if (tokens <= 0 || hidden <= 0) return hipSuccess;
     const int h4 = hidden / 4;
-    const int per_token = (h4 + kCombineThreads - 1) / kCombineThreads;
-    const dim3 grid(unsigned(tokens) * unsigned(per_token)), block(kCombineThreads);
+    const long long n4 = (long long)tokens * h4;
+    const dim3 grid(unsigned((n4 + kCombineThreads - 1) / kCombineThreads)), block(kCombineThreads);
     const size_t dm_bytes = size_t(tokens) * size_t(topk) * size_t(hidden) * 4u;
     if (dm_bytes > (size_t(256) << 20))
-        hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, stream, dm, w, out, topk, h4, per_token);
+        hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, stream, dm, w, out, topk, h4, n4);
     else
-        hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, stream, dm, w, out, topk, h4, per_token);
+        hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, stream, dm, w, out, topk, h4, n4);
     return hipGetLastError();
 }
 
