@@ -1,0 +1,25 @@
+"""bench.py's contract parts that need no GPU: one GPU only (N > 1 exits with
+a message and a non-zero status before touching the device), and the
+options the driver passes."""
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2", "--steps", "3",
+                        "--warmup", "1"], capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2, r.stdout + r.stderr
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in line["error"]
+
+
+def test_options():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"], capture_output=True,
+                       text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 0
+    for opt in ("--gpus", "--steps", "--warmup", "--workload", "--sweep"):
+        assert opt in r.stdout
