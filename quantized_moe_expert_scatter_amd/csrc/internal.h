@@ -14,6 +14,12 @@ constexpr int kMaxChunkRows = 128;  // rows of one chunk = four 32-row MFMA tile
 constexpr int kTileRows = 256;     // weight rows (outputs) per workgroup: 4 waves x 64
 constexpr int kMaxSmallRows = 8;      // chunks of at most this many rows take the small kernel
 constexpr int kSmallActBytes = 32768; // its LDS for the chunk's q8_1 rows
+// A product whose small experts make fewer chunks than this, beside large
+// ones, runs them on the product kernel instead: a launch of a few
+// small-chunk workgroups, each streaming an expert's weights, costs its full
+// latency (about 47 us for gate/up at 8,192 lognormal tokens) where a few
+// more items in the product launch cost next to nothing.
+constexpr int kSmallMinChunks = 96;
 constexpr uint32_t kMagicBits = 0x4B400000u;  // 1.5 * 2^23 as binary32
 
 constexpr size_t align16(size_t x) { return (x + 15) & ~size_t(15); }

@@ -330,28 +330,40 @@ int moe_prefill_plan(const int32_t *ids, int tokens, int topk, int n_expert, int
             members[x].push_back(e);
         }
         const int small[2] = {small_rows_for(p->hidden), small_rows_for(p->n_ff)};
-        int start = 0;
+        int cnt[kXcds], large[2][kXcds], tot_small[2] = {0, 0}, tot_large[2] = {0, 0};
+        std::vector<std::vector<int32_t>> lists(kXcds);
         for (int x = 0; x < kXcds; ++x) {
-            const std::vector<int32_t> list = chunk_list(members[x], p->counts, p->offsets, chunk_rows);
-            const int cnt = int(list.size() / 4);
-            p->xcd_tab[kXcdStart * kXcds + x] = start;
-            p->xcd_tab[kXcdCount * kXcds + x] = cnt;
+            lists[x] = chunk_list(members[x], p->counts, p->offsets, chunk_rows);
+            cnt[x] = int(lists[x].size() / 4);
             for (int q = 0; q < 2; ++q) {
                 // members come largest first: the experts above the small
                 // kernel's row limit are a prefix of the list
-                int large = 0;
+                large[q][x] = 0;
                 for (int e : members[x])
-                    if (p->counts[e] > small[q]) large += (p->counts[e] + chunk_rows - 1) / chunk_rows;
-                p->xcd_tab[(kXcdLarge + 4 * q) * kXcds + x] = start;
-                p->xcd_tab[(kXcdLarge + 4 * q + 1) * kXcds + x] = large;
-                p->xcd_tab[(kXcdSmall + 4 * q) * kXcds + x] = start + large;
-                p->xcd_tab[(kXcdSmall + 4 * q + 1) * kXcds + x] = cnt - large;
-                p->max_large[q] = std::max(p->max_large[q], large);
-                p->max_small[q] = std::max(p->max_small[q], cnt - large);
+                    if (p->counts[e] > small[q]) large[q][x] += (p->counts[e] + chunk_rows - 1) / chunk_rows;
+                tot_large[q] += large[q][x];
+                tot_small[q] += cnt[x] - large[q][x];
             }
-            start += cnt;
-            p->max_xcd_chunks = std::max(p->max_xcd_chunks, cnt);
-            p->dev_chunks.insert(p->dev_chunks.end(), list.begin(), list.end());
+        }
+        // a few small experts beside large ones join the product kernel's view
+        for (int q = 0; q < 2; ++q)
+            if (tot_small[q] < kSmallMinChunks && tot_large[q] > 0)
+                for (int x = 0; x < kXcds; ++x) large[q][x] = cnt[x];
+        int start = 0;
+        for (int x = 0; x < kXcds; ++x) {
+            p->xcd_tab[kXcdStart * kXcds + x] = start;
+            p->xcd_tab[kXcdCount * kXcds + x] = cnt[x];
+            for (int q = 0; q < 2; ++q) {
+                p->xcd_tab[(kXcdLarge + 4 * q) * kXcds + x] = start;
+                p->xcd_tab[(kXcdLarge + 4 * q + 1) * kXcds + x] = large[q][x];
+                p->xcd_tab[(kXcdSmall + 4 * q) * kXcds + x] = start + large[q][x];
+                p->xcd_tab[(kXcdSmall + 4 * q + 1) * kXcds + x] = cnt[x] - large[q][x];
+                p->max_large[q] = std::max(p->max_large[q], large[q][x]);
+                p->max_small[q] = std::max(p->max_small[q], cnt[x] - large[q][x]);
+            }
+            start += cnt[x];
+            p->max_xcd_chunks = std::max(p->max_xcd_chunks, cnt[x]);
+            p->dev_chunks.insert(p->dev_chunks.end(), lists[x].begin(), lists[x].end());
         }
     }
 

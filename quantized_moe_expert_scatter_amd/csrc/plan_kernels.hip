@@ -279,13 +279,24 @@ __device__ void plan_schedule(uint8_t *smem, const int32_t *counts, int n_expert
         aux[PlanAux::base_of(n_expert, e)] = s_base[r];
     }
     if (tid == 0) {
+        // a few small experts beside large ones join the product kernel's
+        // view (the rule of the host plan)
+        bool fold[2];
+        for (int q = 0; q < 2; ++q) {
+            int32_t tot_small = 0, tot_large = 0;
+            for (int x = 0; x < kXcds; ++x) {
+                tot_large += s_listed[1 + q][x];
+                tot_small += s_listed[0][x] - s_listed[1 + q][x];
+            }
+            fold[q] = tot_small < kSmallMinChunks && tot_large > 0;
+        }
         int32_t start = 0;
         for (int x = 0; x < kXcds; ++x) {
             const int32_t cnt = s_listed[0][x];
             xcd_tab[kXcdStart * kXcds + x] = start;
             xcd_tab[kXcdCount * kXcds + x] = cnt;
             for (int q = 0; q < 2; ++q) {
-                const int32_t large = s_listed[1 + q][x];
+                const int32_t large = fold[q] ? cnt : s_listed[1 + q][x];
                 xcd_tab[(kXcdLarge + 4 * q) * kXcds + x] = start;
                 xcd_tab[(kXcdLarge + 4 * q + 1) * kXcds + x] = large;
                 xcd_tab[(kXcdSmall + 4 * q) * kXcds + x] = start + large;
