@@ -47,11 +47,15 @@
 //  * Raw weight and activation bytes are loaded 2-6 stages ahead of their use
 //    (deeper when the chunk has fewer rows and registers allow); every load
 //    is unconditional, so no in-flight register is copied (a copy would make
-//    the compiler wait for every outstanding load).  Loads go through buffer
-//    descriptors (one per expert's weights, one per chunk's rows): a lane's
-//    offset stays in a register, the stage's offset is a scalar, so the
-//    loop computes no 64-bit addresses, and the descriptor's range check
-//    keeps every access inside the expert or the chunk.
+//    the compiler wait for every outstanding load).  Q2_0 loads go through
+//    buffer descriptors (one per expert's weights, one per chunk's rows): a
+//    lane's offset stays in a register, the stage's offset is a scalar, so
+//    the loop computes no 64-bit addresses, and the descriptor's range check
+//    keeps every access inside the expert or the chunk.  The descriptor's
+//    base and range are read from the first lane, which tells the compiler
+//    they are wave-uniform (without that it kept some descriptors in vector
+//    registers and looped over their lanes for every load).  NL4 loads use
+//    clamped 64-bit addresses.
 //  * Work lists are grouped per XCD (workgroup id i runs on XCD i % 8): all
 //    chunks of an expert land on one XCD, so its weight tiles and activation
 //    rows are re-read from that XCD's L2.
@@ -323,6 +327,15 @@ __device__ __forceinline__ void swiglu_store_row(const v16f &g, const v16f &u, u
     }
 }
 
+// A pointer that is the same in every lane, read from the first lane so the
+// compiler keeps it (and what is built from it) in scalar registers.
+__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+    return reinterpret_cast<const uint8_t *>((uint64_t(hi) << 32) | lo);
+}
+
 // The whole K loop of one work item.  Each wave owns 64 weight rows (two
 // 32-row tiles) and runs them against NA 32-row activation tiles (the chunk's
 // rows rounded up; rows past the chunk are never stored).  In the fused
@@ -367,27 +380,32 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
                     (uint32_t(uint8_t(a.codebook[4 * i + 2])) << 16) |
                     (uint32_t(uint8_t(a.codebook[4 * i + 3])) << 24);
     }
-    // the expert's two planes through one buffer descriptor: the lane's
-    // offsets stay in registers, the stage's offset goes in a scalar
+    // Q2_0 items read the expert's two planes (codes, then scales) through
+    // one buffer descriptor: the lane's offsets stay in registers, the
+    // stage's offset is a scalar.
+    constexpr bool BUF = WTYPE == 1;
     const uint32_t codes_bytes = uint32_t(a.out_rows) * uint32_t(nbw) * 16u;
-    const __amdgpu_buffer_rsrc_t wres =
-        __builtin_amdgcn_make_buffer_rsrc((void *)wexp, 0, int(codes_bytes + codes_bytes / 8u), 0x00020000);
+    const uint16_t *wscales = reinterpret_cast<const uint16_t *>(wexp + codes_bytes);
+    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)uniform_ptr(wexp), 0, __builtin_amdgcn_readfirstlane(int(codes_bytes + codes_bytes / 8u)),
+        0x00020000);
     auto wload = [&](int stage, int t) {
         const int s = min(stage, n_stages - 1);
         const int blk = s * (kKS / WB);                      // first block of the stage
         const bool second = WTYPE == 2 && blk + 1 < nbw;
         WRaw w;
-        const int cs = blk * 512, ss = int(codes_bytes) + blk * 64;
-        if constexpr (WTYPE == 1) {
-            w.c0 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(wres, coff[t], cs, 0));
+        if constexpr (BUF) {
+            w.c0 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(wres, coff[t], blk * 512, 0));
             w.c1 = w.c0;
-            w.s = __builtin_amdgcn_raw_buffer_load_b16(wres, 2u * soff[t], ss, 0);
+            w.s = __builtin_amdgcn_raw_buffer_load_b16(wres, 2u * soff[t], int(codes_bytes) + blk * 64, 0);
         } else {
-            const int o1 = second ? 32 : 0;
-            w.c0 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(wres, coff[t], cs, 0));
-            w.c1 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(wres, coff[t], cs + 16 * o1, 0));
-            w.s = uint32_t(__builtin_amdgcn_raw_buffer_load_b16(wres, 2u * soff[t], ss, 0)) |
-                  (uint32_t(__builtin_amdgcn_raw_buffer_load_b16(wres, 2u * soff[t], ss + 2 * o1, 0)) << 16);
+            const uint8_t *codes = wexp + size_t(blk) * 512;
+            const uint16_t *scales = wscales + 32 * blk;
+            const uint32_t o1 = second ? 32u : 0u;       // the next block of the same 32 rows
+            w.c0 = *reinterpret_cast<const uint2 *>(codes + coff[t]);
+            w.c1 = WTYPE == 1 ? w.c0 : *reinterpret_cast<const uint2 *>(codes + coff[t] + 16u * o1);
+            w.s = WTYPE == 1 ? uint32_t(scales[soff[t]])
+                             : uint32_t(scales[soff[t]]) | (uint32_t(scales[soff[t] + o1]) << 16);
         }
         return w;
     };
@@ -397,18 +415,25 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
     const int sblk = tid & 1;
     const uint8_t *abase = a.act + size_t(row0) * arb;
     const uint32_t aoff = uint32_t(min(srow, nrows - 1)) * arb;
-    // the chunk's rows through one descriptor; a block past a row's last one
-    // (a half-filled last stage) reads bytes that are never used, and past the
-    // chunk the descriptor's range check returns zeros
-    const __amdgpu_buffer_rsrc_t ares =
-        __builtin_amdgcn_make_buffer_rsrc((void *)abase, 0, int(uint32_t(nrows) * arb), 0x00020000);
+    // the chunk's rows through one descriptor (Q2_0 items; a stage holds two
+    // whole blocks, and past the chunk the range check returns zeros), else
+    // through clamped, always in-bounds 64-bit addresses
+    const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)uniform_ptr(abase), 0, __builtin_amdgcn_readfirstlane(int(uint32_t(nrows) * arb)), 0x00020000);
     const uint32_t aq = aoff + 32u * uint32_t(sblk), ad = aoff + uint32_t(cols) + 4u * uint32_t(sblk);
     auto aload = [&](int stage) {
         const int s = min(stage, n_stages - 1);
         ARaw r;
-        r.q0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, aq, 64 * s, 0));
-        r.q1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, aq + 16u, 64 * s, 0));
-        r.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ares, ad, 8 * s, 0));
+        if constexpr (BUF) {
+            r.q0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, aq, 64 * s, 0));
+            r.q1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, aq + 16u, 64 * s, 0));
+            r.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ares, ad, 8 * s, 0));
+        } else {
+            const int kb = min(s * 2 + sblk, nb32 - 1);
+            r.q0 = *reinterpret_cast<const uint4 *>(abase + aoff + 32u * kb);
+            r.q1 = *reinterpret_cast<const uint4 *>(abase + aoff + 32u * kb + 16u);
+            r.d = *reinterpret_cast<const float *>(abase + aoff + uint32_t(cols) + 4u * kb);
+        }
         return r;
     };
 
