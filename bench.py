@@ -245,6 +245,8 @@ def main():
     ap.add_argument("--also", default="2k,8k,t128", help="other layers reported alongside")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=6000)
+    ap.add_argument("--cpu-rows-one-core", type=int, default=1000,
+                    help="rows of the 2k layer for the one-core oracle time (when 2k is run)")
     ap.add_argument("--chunk-rows", type=int, default=128)
     ap.add_argument("--sweep", action="store_true",
                     help="instead: the rows-per-expert sweep (768..4096 tokens x lognormal "
@@ -268,6 +270,7 @@ def main():
     main_cfg = layers[args.workload]
     names = [args.workload] + [n for n in args.also.split(",") if n and n != args.workload]
     main_layer = None
+    layer_2k = None
     for name in names:
         cfg = layers[name]
         print(f"[bench] {name}: generating inputs", file=sys.stderr, flush=True)
@@ -301,6 +304,8 @@ def main():
               file=sys.stderr, flush=True)
         if name == args.workload:
             main_layer, main_by, main_ops, main_alu, main_pk = L, by, ops, alu, per_kernel
+        if name == "2k":
+            layer_2k = L
         D.close()
         del D
         torch.cuda.empty_cache()
@@ -330,6 +335,10 @@ def main():
         threads = min(16, os.cpu_count() or 1)
         print(f"[bench] cpu baseline on {threads} threads", file=sys.stderr, flush=True)
         cpu = run_cpu_baseline(main_layer, threads, args.cpu_rows)
+        if layer_2k is not None:
+            # the same chain on one core, at 2,048 tokens
+            print("[bench] cpu baseline on one core, 2k layer", file=sys.stderr, flush=True)
+            cpu["one_core_2k"] = run_cpu_baseline(layer_2k, 1, args.cpu_rows_one_core)
 
     line = {
         "metric": METRIC,

@@ -23,3 +23,17 @@ def test_options():
     assert r.returncode == 0
     for opt in ("--gpus", "--steps", "--warmup", "--workload", "--sweep"):
         assert opt in r.stdout
+
+
+def test_cpu_baseline_leg_on_the_tiny_layer():
+    """The oracle leg times whole experts' rows and scales by rows; on one
+    core as on several it reports the fields the bench line carries."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from quantized_moe_expert_scatter_amd import workloads as wl
+    L = wl.make_layer(wl.CONFIGS["tiny"])
+    for threads in (1, 2):
+        cpu = bench.run_cpu_baseline(L, threads, 40)
+        assert cpu["kind"] == "oracle" and cpu["cores"] == threads
+        assert cpu["unit"] == "effective int8 TOPS" and cpu["value"] > 0 and cpu["ms_per_layer"] > 0
+        assert "of 128 expert-sorted rows" in cpu["sample"]
