@@ -168,6 +168,20 @@ def issue_for(kernel, workload):
     return {k: rec[k] for k in ("valu_busy", "mfma_busy", "cycles_per_valu_instruction", "clock_ghz")}
 
 
+def host_cpu():
+    """The host's CPU model and logical CPU count (for the oracle's timing)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "logical_cpus": os.cpu_count()}
+
+
 def run_cpu_baseline(L, threads, target_rows):
     from oracle import oracle
     cfg = L.cfg
@@ -339,6 +353,7 @@ def main():
             # the same chain on one core, at 2,048 tokens
             print("[bench] cpu baseline on one core, 2k layer", file=sys.stderr, flush=True)
             cpu["one_core_2k"] = run_cpu_baseline(layer_2k, 1, args.cpu_rows_one_core)
+        cpu["host"] = host_cpu()
 
     line = {
         "metric": METRIC,

@@ -37,3 +37,5 @@ def test_cpu_baseline_leg_on_the_tiny_layer():
         assert cpu["kind"] == "oracle" and cpu["cores"] == threads
         assert cpu["unit"] == "effective int8 TOPS" and cpu["value"] > 0 and cpu["ms_per_layer"] > 0
         assert "of 128 expert-sorted rows" in cpu["sample"]
+    host = bench.host_cpu()
+    assert host["logical_cpus"] >= 1 and isinstance(host["model"], str)
