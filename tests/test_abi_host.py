@@ -250,6 +250,15 @@ def test_device_plan_validation_errors():
     assert st(gu=u_gu) == -3
     assert L.moe_prefill_plan_device(DEV_IDS, 8, 2, 4, 64, ctypes.byref(w_gu.struct),
                                      ctypes.byref(w_dn.struct), FAKE_BASE, need, None, None) == -1
+    # the stated limits, each against its neighbour inside the limit, which
+    # passes that check and is refused by the later size check (16 bytes):
+    # fewer than 2^29 rows (an XCD's rows and index share 32 bits) ...
+    assert st(T=(1 << 28), K=2, nb=16) == -1
+    assert st(T=(1 << 28) - 1, K=2, nb=16) == -4
+    # ... and at most 2048 experts (the schedule's LDS arrays)
+    for E, want in ((2049, -1), (2048, -4)):
+        e_gu, e_dn = _weights(wl.small_config("v", 8, 128, 64, E, 2))
+        assert st(E=E, gu=e_gu, dn=e_dn, nb=16) == want
 
 
 def test_missing_library_fails_loudly(tmp_path):
