@@ -94,7 +94,9 @@ typedef enum {
  *             weights in the tiled layout, type | MOE_W_TILED
  *   rows      output features (gate/up: 2*n_ff; down: hidden), % 64 == 0
  *   cols      contraction length (gate/up: hidden; down: n_ff), % 64 (Q2_0)
- *             or % 32 (NL4) == 0
+ *             or % 32 (NL4) == 0; one expert's matrix (rows * cols / block
+ *             * 18 bytes) below 2^31 bytes (MOE_EINVAL beyond: the kernels
+ *             address inside an expert with 32-bit offsets)
  *   n_expert  number of experts
  *   base      device pointer, 16-byte aligned
  *   base_bytes size of the buffer at base (every expert must lie inside it)

@@ -70,6 +70,8 @@ int check_weights(const moe_weights *w, int n_expert, bool tiled) {
     if (t == MOE_W_NL4 && !w->codebook) return MOE_EINVAL;
     if (!aligned16(w->base)) return MOE_EALIGN;
     const size_t per = weight_bytes(t, w->rows, w->cols);
+    // the kernels address inside one expert with 32-bit offsets
+    if (per >= (size_t(1) << 31)) return MOE_EINVAL;
     for (int e = 0; e < n_expert; ++e) {
         if (w->offset[e] & 15u) return MOE_EALIGN;
         if (w->offset[e] > w->base_bytes || w->base_bytes - w->offset[e] < per) return MOE_ESIZE;

@@ -222,6 +222,14 @@ def test_pack_validation_errors():
     _, w_dn = _weights(cfg, tiled=False, down_type=2)
     w_dn.struct.codebook = None
     assert _pack_status(w_dn, DST, w_dn.struct.base_bytes) == -1
+    # one expert's matrix must stay below 2^31 bytes (32-bit offsets inside an
+    # expert); just below, the descriptor passes and the small destination is
+    # what is refused
+    for cols, want in ((131072, -1), (114688, -4)):
+        per = _lib.moe_weight_bytes(1, 65536, cols)
+        assert (per >= 1 << 31) == (want == -1)
+        big = _lib.Weights(1, 65536, cols, 1, FAKE_BASE, per, np.zeros(1, dtype=np.uint64))
+        assert _pack_status(big, DST, 16) == want
 
 
 def test_device_plan_validation_errors():
