@@ -39,3 +39,27 @@ def test_cpu_baseline_leg_on_the_tiny_layer():
         assert "of 128 expert-sorted rows" in cpu["sample"]
     host = bench.host_cpu()
     assert host["logical_cpus"] >= 1 and isinstance(host["model"], str)
+
+
+def test_counter_records_apply_only_to_their_source(tmp_path, monkeypatch):
+    """traffic and issue figures come from committed counter records, and only
+    while the kernel file they were taken on is unchanged."""
+    import hashlib
+    sys.path.insert(0, ROOT)
+    import bench
+    (tmp_path / "profiles").mkdir()
+    src = tmp_path / "k.hip"
+    src.write_text("// kernel\n")
+    sha = hashlib.sha1(src.read_bytes()).hexdigest()
+    (tmp_path / "profiles" / "traffic_k_w.json").write_text(
+        json.dumps({"source_sha1": sha, "bytes_per_launch": 1234}))
+    (tmp_path / "profiles" / "issue_k_w.json").write_text(json.dumps(
+        {"source_sha1": sha, "valu_busy": 0.8, "mfma_busy": 0.3, "cycles_per_valu_instruction": 4.0,
+         "clock_ghz": 2.0}))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setitem(bench.KERNEL_SOURCES, "k", "k.hip")
+    assert bench.traffic_for("k", "w") == 1234
+    assert bench.issue_for("k", "w")["valu_busy"] == 0.8
+    assert bench.traffic_for("k", "other") is None and bench.issue_for("k", "other") is None
+    src.write_text("// kernel, changed\n")
+    assert bench.traffic_for("k", "w") is None and bench.issue_for("k", "w") is None
