@@ -142,17 +142,29 @@ def time_plans(D, L, chunk_rows, reps=5):
     return {"host_ms": round(float(np.median(host)), 3), "device_ms": round(float(np.median(dev)), 3)}
 
 
+def _load(path):
+    with open(path) as f:
+        return json.load(f)
+
+
+def _record_sha(path):
+    return _load(path).get("source_sha1")
+
+
+def _source_sha(kernel):
+    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as f:
+        return hashlib.sha1(f.read()).hexdigest()
+
+
 def traffic_for(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source (else None)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path))
-    src = open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb").read()
-    if rec.get("source_sha1") != hashlib.sha1(src).hexdigest():
+    if _record_sha(path) != _source_sha(kernel):
         return None
-    return rec.get("bytes_per_launch")
+    return _load(path).get("bytes_per_launch")
 
 
 def issue_for(kernel, workload):
@@ -161,10 +173,9 @@ def issue_for(kernel, workload):
     path = os.path.join(ROOT, "profiles", f"issue_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path))
-    src = open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb").read()
-    if rec.get("source_sha1") != hashlib.sha1(src).hexdigest():
+    if _record_sha(path) != _source_sha(kernel):
         return None
+    rec = _load(path)
     return {k: rec[k] for k in ("valu_busy", "mfma_busy", "cycles_per_valu_instruction", "clock_ghz")}
 
 
