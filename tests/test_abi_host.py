@@ -21,7 +21,8 @@ FAKE_BASE = 1 << 20          # an aligned stand-in address: host-only plans neve
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    with open(HEADER) as f:
+        text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)
     return sorted(set(n for n in names if n not in ("if", "defined")))
