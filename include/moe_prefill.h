@@ -76,7 +76,9 @@ typedef enum {
     MOE_EFORMAT = -3,  /* unknown weight type, or dims not a multiple of the block */
     MOE_ESIZE = -4,    /* a caller buffer is smaller than the size query demands */
     MOE_EHIP = -5,     /* HIP reported an error while enqueueing */
-    MOE_ESTATE = -6    /* the plan was built without a device workspace */
+    MOE_ESTATE = -6,   /* the plan was built without a device workspace */
+    MOE_ENOMEM = -7    /* host memory ran out (plans, their queries, the pack's checks);
+                          nothing was launched and no plan was returned */
 } moe_status;
 
 typedef enum {

@@ -21,7 +21,7 @@ MOE_W_TILED = 0x100
 MOE_W_GU_INTERLEAVED = 0x200
 
 STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EALIGN", -3: "MOE_EFORMAT",
-          -4: "MOE_ESIZE", -5: "MOE_EHIP", -6: "MOE_ESTATE"}
+          -4: "MOE_ESIZE", -5: "MOE_EHIP", -6: "MOE_ESTATE", -7: "MOE_ENOMEM"}
 
 # every symbol include/moe_prefill.h declares
 EXPORTS = ["moe_q8_1_bytes", "moe_weight_bytes", "moe_weights_pack", "moe_plan_device_bytes",

@@ -13,6 +13,7 @@
 
 #include <algorithm>
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -100,10 +101,17 @@ int check_plan_args(int tokens, int topk, int n_expert, int chunk_rows, const mo
     return MOE_OK;
 }
 
-moe_plan *new_plan(int tokens, int topk, int n_expert, int chunk_rows, const moe_weights *w_gu,
-                   const moe_weights *w_down) {
-    moe_plan *p = new (std::nothrow) moe_plan;
-    if (!p) return nullptr;
+// A plan under construction: destroyed (waiting for its upload) unless released.
+struct PlanDeleter {
+    void operator()(moe_plan *p) const { moe_plan_destroy(p); }
+};
+using PlanPtr = std::unique_ptr<moe_plan, PlanDeleter>;
+
+// Host allocations here and below throw std::bad_alloc when memory runs out;
+// the exported functions turn that into MOE_ENOMEM (guarded, below).
+PlanPtr new_plan(int tokens, int topk, int n_expert, int chunk_rows, const moe_weights *w_gu,
+                 const moe_weights *w_down) {
+    PlanPtr p(new moe_plan);
     p->tokens = tokens; p->topk = topk; p->n_expert = n_expert; p->chunk_rows = chunk_rows;
     p->rows = tokens * topk; p->hidden = w_gu->cols; p->n_ff = w_gu->rows / 2;
     p->gu = *w_gu; p->dn = *w_down;
@@ -167,9 +175,13 @@ class StagingPool {
         *cap = c;
         return ptr;
     }
-    void give(void *ptr, size_t cap) {
+    void give(void *ptr, size_t cap) noexcept {
         std::lock_guard<std::mutex> g(m_);
-        free_.emplace_back(cap, ptr);
+        try {
+            free_.emplace_back(cap, ptr);
+        } catch (...) {
+            (void)hipHostFree(ptr);        // no room to keep it: free it (waits for the device)
+        }
     }
 
   private:
@@ -210,6 +222,16 @@ int upload(moe_plan *p, size_t begin, size_t end, void *stream, Fill fill, Then 
     return launched == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
+// Runs an exported function's body; no exception crosses the C boundary.
+template <class F>
+int guarded(F &&body) noexcept {
+    try {
+        return body();
+    } catch (...) {
+        return MOE_ENOMEM;
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -221,7 +243,7 @@ size_t moe_q8_1_bytes(int rows, int cols) {
 
 size_t moe_weight_bytes(int type, int rows, int cols) { return weight_bytes(type, rows, cols); }
 
-int moe_weights_pack(const moe_weights *w, void *dst, size_t dst_bytes, void *stream) {
+static int moe_weights_pack_impl(const moe_weights *w, void *dst, size_t dst_bytes, void *stream) {
     if (!w || !dst) return MOE_EINVAL;
     const int st = check_weights(w, w->n_expert, false);
     if (st) return st;
@@ -259,6 +281,10 @@ int moe_weights_pack(const moe_weights *w, void *dst, size_t dst_bytes, void *st
     return MOE_OK;
 }
 
+int moe_weights_pack(const moe_weights *w, void *dst, size_t dst_bytes, void *stream) {
+    return guarded([&] { return moe_weights_pack_impl(w, dst, dst_bytes, stream); });
+}
+
 size_t moe_plan_device_bytes(int tokens, int topk, int n_expert, int chunk_rows) {
     if (tokens < 0 || topk <= 0 || n_expert <= 0 || chunk_rows <= 0 || chunk_rows > kMaxChunkRows)
         return 0;
@@ -272,6 +298,7 @@ const char *moe_status_string(int s) {
         case MOE_EALIGN: return "pointer or offset not 16-byte aligned";
         case MOE_EFORMAT: return "unsupported weight format or dimension";
         case MOE_ESIZE: return "buffer too small";
+        case MOE_ENOMEM: return "host memory exhausted";
         case MOE_EHIP: return "HIP error";
         case MOE_ESTATE: return "plan has no device workspace";
         default: return "unknown status";
@@ -279,9 +306,10 @@ const char *moe_status_string(int s) {
 }
 
 
-int moe_prefill_plan(const int32_t *ids, int tokens, int topk, int n_expert, int chunk_rows,
-                     const moe_weights *w_gu, const moe_weights *w_down, void *plan_dev,
-                     size_t plan_dev_bytes, void *stream, moe_plan **out) {
+static int moe_prefill_plan_impl(const int32_t *ids, int tokens, int topk, int n_expert,
+                                 int chunk_rows, const moe_weights *w_gu, const moe_weights *w_down,
+                                 void *plan_dev, size_t plan_dev_bytes, void *stream,
+                                 moe_plan **out) {
     if (!out) return MOE_EINVAL;
     *out = nullptr;
     int st = check_plan_args(tokens, topk, n_expert, chunk_rows, w_gu, w_down);
@@ -295,8 +323,7 @@ int moe_prefill_plan(const int32_t *ids, int tokens, int topk, int n_expert, int
         if (!aligned16(plan_dev)) return MOE_EALIGN;
         if (plan_dev_bytes < L.total) return MOE_ESIZE;
     }
-    moe_plan *p = new_plan(tokens, topk, n_expert, chunk_rows, w_gu, w_down);
-    if (!p) return MOE_EINVAL;
+    PlanPtr p = new_plan(tokens, topk, n_expert, chunk_rows, w_gu, w_down);
 
     // counting sort by expert, stable in t*K+k
     p->counts.assign(n_expert, 0);
@@ -372,7 +399,7 @@ int moe_prefill_plan(const int32_t *ids, int tokens, int topk, int n_expert, int
     if (plan_dev) {
         p->plan_dev = plan_dev;
         // the sections after dn_off are the device-built plan's own
-        st = upload(p, 0, L.counts, stream,
+        st = upload(p.get(), 0, L.counts, stream,
                     [&](uint8_t *s) {
                         std::memcpy(s + L.perm, p->perm.data(), size_t(R) * 4);
                         std::memcpy(s + L.inv, p->inv.data(), size_t(R) * 4);
@@ -382,18 +409,25 @@ int moe_prefill_plan(const int32_t *ids, int tokens, int topk, int n_expert, int
                         std::memcpy(s + L.dn_off, p->dn_off.data(), size_t(n_expert) * 8);
                     },
                     [](hipStream_t) { return hipSuccess; });
-        if (st) {
-            moe_plan_destroy(p);
-            return st;
-        }
+        if (st) return st;
     }
-    *out = p;
+    *out = p.release();
     return MOE_OK;
 }
 
-int moe_prefill_plan_device(const int32_t *ids_dev, int tokens, int topk, int n_expert,
-                            int chunk_rows, const moe_weights *w_gu, const moe_weights *w_down,
-                            void *plan_dev, size_t plan_dev_bytes, void *stream, moe_plan **out) {
+int moe_prefill_plan(const int32_t *ids, int tokens, int topk, int n_expert, int chunk_rows,
+                     const moe_weights *w_gu, const moe_weights *w_down, void *plan_dev,
+                     size_t plan_dev_bytes, void *stream, moe_plan **out) {
+    return guarded([&] {
+        return moe_prefill_plan_impl(ids, tokens, topk, n_expert, chunk_rows, w_gu, w_down, plan_dev,
+                                     plan_dev_bytes, stream, out);
+    });
+}
+
+static int moe_prefill_plan_device_impl(const int32_t *ids_dev, int tokens, int topk,
+                                        int n_expert, int chunk_rows, const moe_weights *w_gu,
+                                        const moe_weights *w_down, void *plan_dev,
+                                        size_t plan_dev_bytes, void *stream, moe_plan **out) {
     if (!out) return MOE_EINVAL;
     *out = nullptr;
     int st = check_plan_args(tokens, topk, n_expert, chunk_rows, w_gu, w_down);
@@ -404,8 +438,7 @@ int moe_prefill_plan_device(const int32_t *ids_dev, int tokens, int topk, int n_
     if ((ids_dev && !aligned16(ids_dev)) || !aligned16(plan_dev)) return MOE_EALIGN;
     const PlanLayout L = plan_layout(tokens, topk, n_expert, chunk_rows);
     if (plan_dev_bytes < L.total) return MOE_ESIZE;
-    moe_plan *p = new_plan(tokens, topk, n_expert, chunk_rows, w_gu, w_down);
-    if (!p) return MOE_EINVAL;
+    PlanPtr p = new_plan(tokens, topk, n_expert, chunk_rows, w_gu, w_down);
     p->device_built = true;
     p->plan_dev = plan_dev;
     // per-XCD list lengths are known only on the device: launches take the
@@ -414,7 +447,7 @@ int moe_prefill_plan_device(const int32_t *ids_dev, int tokens, int topk, int n_
     p->max_xcd_chunks = max_chunks(p->rows, n_expert, chunk_rows);
     for (int q = 0; q < 2; ++q) p->max_large[q] = p->max_small[q] = p->max_xcd_chunks;
     // the two weight offset tables go up from the host, the rest is built there
-    st = upload(p, L.gu_off, L.counts, stream,
+    st = upload(p.get(), L.gu_off, L.counts, stream,
                 [&](uint8_t *s) {
                     std::memcpy(s + L.gu_off, p->gu_off.data(), size_t(n_expert) * 8);
                     std::memcpy(s + L.dn_off, p->dn_off.data(), size_t(n_expert) * 8);
@@ -424,16 +457,22 @@ int moe_prefill_plan_device(const int32_t *ids_dev, int tokens, int topk, int n_
                                               small_rows_for(p->hidden), small_rows_for(p->n_ff),
                                               static_cast<uint8_t *>(plan_dev), L, hs);
                 });
-    if (st) {
-        moe_plan_destroy(p);
-        return st;
-    }
-    *out = p;
+    if (st) return st;
+    *out = p.release();
     return MOE_OK;
 }
 
-int moe_plan_query(const moe_plan *p, int *rows, int *n_chunks, int32_t *counts, int32_t *offsets,
-                   int32_t *perm, int32_t *chunks) {
+int moe_prefill_plan_device(const int32_t *ids_dev, int tokens, int topk, int n_expert,
+                            int chunk_rows, const moe_weights *w_gu, const moe_weights *w_down,
+                            void *plan_dev, size_t plan_dev_bytes, void *stream, moe_plan **out) {
+    return guarded([&] {
+        return moe_prefill_plan_device_impl(ids_dev, tokens, topk, n_expert, chunk_rows, w_gu, w_down,
+                                            plan_dev, plan_dev_bytes, stream, out);
+    });
+}
+
+static int moe_plan_query_impl(const moe_plan *p, int *rows, int *n_chunks, int32_t *counts,
+                               int32_t *offsets, int32_t *perm, int32_t *chunks) {
     if (!p) return MOE_EINVAL;
     if (p->device_built) {
         // read the device-built plan back (waits for it)
@@ -468,6 +507,12 @@ int moe_plan_query(const moe_plan *p, int *rows, int *n_chunks, int32_t *counts,
     if (perm) std::copy(p->perm.begin(), p->perm.end(), perm);
     if (chunks) std::copy(p->chunks.begin(), p->chunks.end(), chunks);
     return MOE_OK;
+}
+
+int moe_plan_query(const moe_plan *p, int *rows, int *n_chunks, int32_t *counts, int32_t *offsets,
+                   int32_t *perm, int32_t *chunks) {
+    return guarded(
+        [&] { return moe_plan_query_impl(p, rows, n_chunks, counts, offsets, perm, chunks); });
 }
 
 void moe_plan_destroy(moe_plan *p) {

@@ -287,3 +287,18 @@ def test_missing_library_fails_loudly(tmp_path):
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "is missing" in r.stdout
+
+
+def test_every_status_has_a_name_and_a_message():
+    """Each status the header declares is named by the binding and described
+    by moe_status_string (out-of-memory included: the allocating entry points
+    return it instead of letting an exception cross the C boundary)."""
+    with open(HEADER) as f:
+        text = f.read()
+    declared = {int(v): n for n, v in re.findall(r"\b(MOE_(?:OK|E[A-Z]+))\s*=\s*(-?\d+)", text)}
+    assert declared[-7] == "MOE_ENOMEM"
+    assert _lib.STATUS == declared
+    L = _lib.lib()
+    for code in declared:
+        assert L.moe_status_string(code).decode() != "unknown status", code
+    assert L.moe_status_string(-99).decode() == "unknown status"
