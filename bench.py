@@ -1,14 +1,21 @@
 """Benchmark of the prefill routed-expert product on one MI355X.
 
-One step = one layer's whole routed-expert product: quantize_scatter,
-expert_gate_up, swiglu_q8 and expert_down (four launches) over inputs already
-resident in HBM.  The plan (host counting sort + one upload) is built once
+One step = one layer's whole routed-expert product in three launches
+(quantize_scatter; the gate/up product with swiglu and q8_1 of H fused into
+its epilogue; the down product) over inputs already resident in HBM.  The
+plan (host counting sort + one upload, or the device-built plan) is built once
 outside the timed region and timed separately.
 
+Every layer's inputs are generated and uploaded before any timing; all layers
+are warmed up together; the headline layer is then timed over exactly
+--steps steps between two synchronizations (value, ms_per_step), and every
+layer in every form (three launches, four launches with GU in memory, and
+with the combine) over --rounds interleaved rounds, reported as medians.
+
 Prints ONE JSON line: value = effective int8 TOPS of the 16,384-token layer
-(2 x useful MACs / time), ms_per_step = ms per layer; the 2k, 8k and t128
-layers are reported alongside, the roofline of the dominant kernel, and the
-oracle timed on a bounded sample of rows on the host cores.
+(2 x useful MACs / time), ms_per_step = ms per layer; the 2k, 8k, t128 and
+2k_nl4 layers alongside, the roofline of the dominant kernel and of the
+layer, and the oracle timed on a bounded sample of rows on the host cores.
 """
 from __future__ import annotations
 
@@ -30,8 +37,10 @@ METRIC = "ms/layer + effective int8 TOPS (512 experts, top-10) at 2K/8K/16K toke
 # Ti at 2,048 and 16,384 tokens (ms per layer)
 PAGES_MS = {"2k": 6.61, "16k": 37.15}
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
-# the products run on fp16 matrix cores (int8 values and 2/4-bit weights are
-# exact in fp16): dense fp16 MFMA peak
+# the method's products are int8 contractions: dense int8 MFMA peak of MI355X
+MFMA_I8_PEAK_TOPS = 5000.0
+# they run on fp16 matrix cores here (int8 values and 2/4-bit weights are
+# exact in fp16): dense fp16 MFMA peak, reported alongside
 MFMA_F16_PEAK_TFLOPS = 2500.0
 # fp32 FMA on the vector ALU, MI355X's published rate: 256 CU x 4 SIMD x 32
 # lanes per clock x 2 flop x 2.4 GHz = 157.3 TFLOP/s.  That rate counts the
@@ -83,20 +92,26 @@ def algorithmic(cfg, counts):
     return by, ops, alu
 
 
-def time_layer(D, steps, warmup, fused=True, combine=False):
+def _forms(D, form):
+    """(kernel names, launch callables) of one step in the given form."""
+    if form == "fused":
+        return list(KERNELS), [D.quantize_scatter, D.expert_gate_up_swiglu_q8, D.expert_down]
+    if form == "four":
+        return list(KERNELS_4), [D.quantize_scatter, D.expert_gate_up, D.swiglu_q8, D.expert_down]
+    return (list(KERNELS) + ["moe_combine"],
+            [D.quantize_scatter, D.expert_gate_up_swiglu_q8, D.expert_down, D.combine])
+
+
+def time_layer(D, steps, warmup, form="fused"):
+    """The contract's timing: warm-up steps, then exactly `steps` steps between
+    two synchronizations; HIP events on the launch stream around every kernel.
+    Returns (ms per step over the bracket, mean ms per kernel)."""
     import torch
     stream = torch.cuda.current_stream()
-    if fused:
-        names, fns = list(KERNELS), [D.quantize_scatter, D.expert_gate_up_swiglu_q8, D.expert_down]
-    else:
-        names, fns = list(KERNELS_4), [D.quantize_scatter, D.expert_gate_up, D.swiglu_q8, D.expert_down]
-    if combine:
-        names.append("moe_combine")
-        fns.append(D.combine)
+    names, fns = _forms(D, form)
     for _ in range(warmup):
         for f in fns:
             f()
-    torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -113,6 +128,34 @@ def time_layer(D, steps, warmup, fused=True, combine=False):
     per_kernel = {k: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]))
                   for i, k in enumerate(names)}
     return total_ms / steps, per_kernel
+
+
+def interleaved_medians(devs, rounds, forms=("fused", "four", "combine")):
+    """The pages' protocol for comparing configurations: one step of every
+    (layer, form) per round, rounds repeated, the median over rounds of each
+    (layer, form) and of each of its kernels.  devs: {name: DeviceLayer}."""
+    import torch
+    stream = torch.cuda.current_stream()
+    order = [(n, f) for n in devs for f in forms]
+    rec = {k: [] for k in order}
+    for _ in range(rounds):
+        for key in order:
+            names, fns = _forms(devs[key[0]], key[1])
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+            ev[0].record(stream)
+            for i, f in enumerate(fns):
+                f()
+                ev[i + 1].record(stream)
+            rec[key].append((names, ev))
+    torch.cuda.synchronize()
+    out = {}
+    for key, samples in rec.items():
+        names = samples[0][0]
+        step = [ev[0].elapsed_time(ev[-1]) for _, ev in samples]
+        kern = {k: float(np.median([ev[i].elapsed_time(ev[i + 1]) for _, ev in samples]))
+                for i, k in enumerate(names)}
+        out[key] = (float(np.median(step)), kern)
+    return out
 
 
 def time_plans(D, L, chunk_rows, reps=5):
@@ -222,21 +265,56 @@ def run_cpu_baseline(L, threads, target_rows):
                       f"scaled by rows"}
 
 
+def build_layers(names, layers, args, wl, DeviceLayer, torch, keep=()):
+    """Every layer's seeded inputs generated and resident in HBM before any
+    timing starts.  Returns {name: (cfg, host Layer or None, DeviceLayer,
+    expert row counts, setup seconds)}; host inputs are kept only for `keep`."""
+    out = {}
+    for name in names:
+        cfg = layers[name]
+        print(f"[bench] {name}: generating inputs", file=sys.stderr, flush=True)
+        L = wl.make_layer(cfg)
+        t0 = time.perf_counter()
+        D = DeviceLayer(L.x, L.ids, L.w_gu, L.w_down, chunk_rows=args.chunk_rows, route_w=L.route_w)
+        torch.cuda.synchronize()
+        setup_s = time.perf_counter() - t0
+        counts = D.plan.query()[0]
+        out[name] = (cfg, L if name in keep else None, D, counts, setup_s)
+    return out
+
+
+def warm(devs, steps):
+    """Untimed steps of every layer, interleaved, until the clock has settled."""
+    import torch
+    for _ in range(steps):
+        for D in devs.values():
+            for f in _forms(D, "fused")[1]:
+                f()
+    torch.cuda.synchronize()
+
+
+def layer_bytes(cfg, counts):
+    """The layer's algorithmic HBM bytes as the method moves them (each
+    counted once: X read, Xq write and read, GU write and read, Hq write and
+    read, Dm write, the touched experts' weights), and the bytes of the path
+    this library runs (GU never stored)."""
+    by, _, _ = algorithmic(cfg, counts)
+    method = sum(by[k] for k in KERNELS_4)
+    return method, sum(by[k] for k in KERNELS)
+
+
 def run_sweep(args, wl, DeviceLayer, torch):
     """ms/layer and effective TOPS over the sweep's layers, three- and
-    four-launch forms, with rows per expert and chunks per launch."""
+    four-launch forms, medians of interleaved rounds."""
+    built = build_layers(list(wl.SWEEP), wl.SWEEP, args, wl, DeviceLayer, torch)
+    devs = {n: v[2] for n, v in built.items()}
+    warm(devs, args.warmup)
+    med = interleaved_medians(devs, args.rounds, forms=("fused", "four"))
     out = {}
-    for name, cfg in wl.SWEEP.items():
-        print(f"[sweep] {name}: generating inputs", file=sys.stderr, flush=True)
-        L = wl.make_layer(cfg)
-        D = DeviceLayer(L.x, L.ids, L.w_gu, L.w_down, chunk_rows=args.chunk_rows,
-                        route_w=L.route_w)
-        torch.cuda.synchronize()
-        counts, _, _, chunks = D.plan.query()
-        n_chunks = chunks.shape[0]
-        steps = max(5, args.steps // 2)
-        ms, pk = time_layer(D, steps, args.warmup)
-        ms4, pk4 = time_layer(D, steps, args.warmup, fused=False)
+    for name, (cfg, _, D, counts, _) in built.items():
+        n_chunks = D.plan.query()[3].shape[0]
+        ms, pk = med[name, "fused"]
+        ms4, pk4 = med[name, "four"]
         _, ops, _ = algorithmic(cfg, counts)
         useful = ops["expert_gate_up"] + ops["expert_down"]
         used = counts[counts > 0]
@@ -250,24 +328,59 @@ def run_sweep(args, wl, DeviceLayer, torch):
                      "four_launch_per_kernel_ms": {k: round(v, 4) for k, v in pk4.items()}}
         print(f"[sweep] {name}: {ms:.3f} ms (four-launch {ms4:.3f}) {out[name]['tops']} TOPS",
               file=sys.stderr, flush=True)
-        D.close()
-        del D
-        torch.cuda.empty_cache()
+    for v in built.values():
+        v[2].close()
     print(json.dumps({"metric": "ms/layer over the rows-per-expert sweep", "unit": "ms",
-                      "n_gpus": 1, "chunk_rows": args.chunk_rows, "layers": out}), flush=True)
+                      "n_gpus": 1, "chunk_rows": args.chunk_rows,
+                      "timing": f"median of {args.rounds} interleaved rounds after {args.warmup} "
+                                f"warm-up steps of every layer",
+                      "layers": out}), flush=True)
+
+
+def roofline(dom, by, ops, alu, pk, workload, cfg, counts, ms_layer):
+    """The dominant kernel against the int8 matrix-core peak (the method's
+    int8 operations: 2 x useful MACs) and the HBM peak (its algorithmic
+    bytes), with the fp16 matrix-core peak it actually runs on and the vector
+    ALU alongside; and the whole layer against HBM."""
+    t = pk[dom] * 1e-3
+    fr = {"hbm": (by[dom] / t / 1e9, HBM_PEAK_GBS, "GB/s")}
+    if dom in ops:
+        fr["mfma"] = (ops[dom] / t / 1e12, MFMA_I8_PEAK_TOPS, "TOP/s (int8)")
+    bound = max(fr, key=lambda k: fr[k][0] / fr[k][1])
+    if dom in ops:
+        fr["mfma_fp16"] = (ops[dom] / t / 1e12, MFMA_F16_PEAK_TFLOPS, "TFLOP/s (fp16)")
+        fr["alu"] = (alu[dom] / t / 1e12, VALU_F32_PEAK_TFLOPS, "TFLOP/s (fp32 vector)")
+    ach, peak, unit = fr[bound]
+    method_bytes, path_bytes = layer_bytes(cfg, counts)
+    s = ms_layer * 1e-3
+    return {"kernel": dom, "bound": bound, "achieved": round(ach, 1), "peak": round(peak, 1),
+            "unit": unit, "frac": round(ach / peak, 3),
+            "traffic": traffic_for(dom, workload),
+            # what the counters say binds it: the share of SIMD cycles its VALU
+            # and its matrix cores are busy (rocprofv3, committed summary)
+            "issue": issue_for(dom, workload),
+            "algorithmic_bytes_per_launch": int(by[dom]),
+            "other_bounds": {k: {"achieved": round(v[0], 1), "peak": round(v[1], 1), "unit": v[2],
+                                 "frac": round(v[0] / v[1], 3)} for k, v in fr.items() if k != bound},
+            "layer_hbm": {"algorithmic_bytes": int(method_bytes),
+                          "achieved_gbs": round(method_bytes / s / 1e9, 1),
+                          "frac": round(method_bytes / s / 1e9 / HBM_PEAK_GBS, 3),
+                          "path_bytes": int(path_bytes),
+                          "path_frac": round(path_bytes / s / 1e9 / HBM_PEAK_GBS, 3)}}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # the clock needs tens of ms of load to settle after the host-side input
-    # generation between layers: 5 warm-up steps read 0.63 ms at 2,048 tokens
-    # against 0.56 in steady state
+    # the clock needs tens of ms of steady load to settle: 5 warm-up steps read
+    # 0.63 ms at 2,048 tokens against 0.56 in steady state
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--rounds", type=int, default=15,
+                    help="interleaved rounds whose medians give every layer's ms (the pages' protocol)")
     ap.add_argument("--workload", default="16k",
-                    help="tiny | 2k | 8k | 16k | t128, or a sweep layer sw<T>_<ln0.5|ln1.0|flat32>")
-    ap.add_argument("--also", default="2k,8k,t128", help="other layers reported alongside")
+                    help="tiny | 2k | 8k | 16k | t128 | 2k_nl4, or a sweep layer sw<T>_<ln0.5|ln1.0|flat32>")
+    ap.add_argument("--also", default="2k,8k,t128,2k_nl4", help="other layers reported alongside")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=6000)
     ap.add_argument("--cpu-rows-one-core", type=int, default=1000,
@@ -278,7 +391,7 @@ def main():
                          "sigma 0.5 / 1.0 and flat 32-row routing), one JSON line of ms/layer")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1"}))
         sys.exit(2)
 
     import torch
@@ -291,89 +404,73 @@ def main():
         run_sweep(args, wl, DeviceLayer, torch)
         return
     layers = {**wl.CONFIGS, **wl.SWEEP}
-    results = {}
-    main_cfg = layers[args.workload]
     names = [args.workload] + [n for n in args.also.split(",") if n and n != args.workload]
-    main_layer = None
-    layer_2k = None
-    for name in names:
-        cfg = layers[name]
-        print(f"[bench] {name}: generating inputs", file=sys.stderr, flush=True)
-        L = wl.make_layer(cfg)
-        t0 = time.perf_counter()
-        D = DeviceLayer(L.x, L.ids, L.w_gu, L.w_down, chunk_rows=args.chunk_rows,
-                        route_w=L.route_w)
-        torch.cuda.synchronize()
-        setup_s = time.perf_counter() - t0
-        counts = D.plan.query()[0]
-        steps = args.steps if name == args.workload else max(5, args.steps // 5)
-        ms, per_kernel = time_layer(D, steps, args.warmup)
-        ms4, per_kernel4 = time_layer(D, max(3, steps // 5), 1, fused=False)
-        msc, per_kernelc = time_layer(D, max(3, steps // 5), 1, combine=True)
+    built = build_layers(names, layers, args, wl, DeviceLayer, torch, keep=(args.workload, "2k"))
+    devs = {n: v[2] for n, v in built.items()}
+    main_cfg, main_layer, main_dev, main_counts, _ = built[args.workload]
+
+    # warm-up of every layer, then the contract's timed region on the headline layer
+    print(f"[bench] warm-up: {args.warmup} steps of each layer", file=sys.stderr, flush=True)
+    warm(devs, args.warmup)
+    ms_main, pk_main = time_layer(main_dev, args.steps, 0)
+    print(f"[bench] {args.workload}: {ms_main:.4f} ms/layer over {args.steps} steps {pk_main}",
+          file=sys.stderr, flush=True)
+    # every layer and form, medians over interleaved rounds
+    med = interleaved_medians(devs, args.rounds)
+    results = {}
+    for name, (cfg, _, D, counts, setup_s) in built.items():
         by, ops, alu = algorithmic(cfg, counts)
         useful_ops = ops["expert_gate_up"] + ops["expert_down"]
+        ms, pk = med[name, "fused"]
+        ms4, pk4 = med[name, "four"]
+        msc, pkc = med[name, "combine"]
         step_bytes = sum(by[k] for k in KERNELS)
+        method_bytes, _ = layer_bytes(cfg, counts)
         results[name] = {"ms_per_layer": round(ms, 4), "tops": round(useful_ops / (ms * 1e-3) / 1e12, 1),
-                         "per_kernel_ms": {k: round(v, 4) for k, v in per_kernel.items()},
+                         "per_kernel_ms": {k: round(v, 4) for k, v in pk.items()},
                          "algorithmic_bytes": int(step_bytes),
                          "hbm_floor_ms": round(step_bytes / (HBM_PEAK_GBS * 1e9) * 1e3, 4),
+                         "layer_hbm_frac": round(method_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3),
                          "four_launch": {"ms_per_layer": round(ms4, 4),
-                                         "per_kernel_ms": {k: round(v, 4) for k, v in per_kernel4.items()}},
+                                         "per_kernel_ms": {k: round(v, 4) for k, v in pk4.items()}},
                          "with_combine": {"ms_per_layer": round(msc, 4),
-                                          "combine_ms": round(per_kernelc["moe_combine"], 4),
+                                          "combine_ms": round(pkc["moe_combine"], 4),
                                           "combine_gbs": round(by["moe_combine"] /
-                                                               (per_kernelc["moe_combine"] * 1e-3) / 1e9, 1)},
-                         "plan": time_plans(D, L, args.chunk_rows),
-                         "steps": steps, "setup_s": round(setup_s, 2)}
-        print(f"[bench] {name}: {ms:.3f} ms/layer {results[name]['tops']} TOPS {per_kernel}",
+                                                               (pkc["moe_combine"] * 1e-3) / 1e9, 1)},
+                         "setup_s": round(setup_s, 2)}
+        print(f"[bench] {name}: median {ms:.4f} ms/layer {results[name]['tops']} TOPS {pk}",
               file=sys.stderr, flush=True)
-        if name == args.workload:
-            main_layer, main_by, main_ops, main_alu, main_pk = L, by, ops, alu, per_kernel
-        if name == "2k":
-            layer_2k = L
-        D.close()
-        del D
-        torch.cuda.empty_cache()
+    for name, (cfg, L, D, counts, _) in built.items():
+        results[name]["plan"] = time_plans(D, L if L is not None else wl.make_layer(cfg), args.chunk_rows)
 
     m = results[args.workload]
-    # roofline of the dominant kernel (the one with the largest share of the step)
-    dom = max(main_pk, key=main_pk.get)
-    t = main_pk[dom] * 1e-3
-    fr = {"hbm": (main_by[dom] / t / 1e9, HBM_PEAK_GBS, "GB/s")}
-    if dom in main_ops:
-        fr["mfma"] = (main_ops[dom] / t / 1e12, MFMA_F16_PEAK_TFLOPS, "TFLOP/s")
-        fr["alu"] = (main_alu[dom] / t / 1e12, VALU_F32_PEAK_TFLOPS, "TFLOP/s")
-    bound = max(fr, key=lambda k: fr[k][0] / fr[k][1])
-    ach, peak, unit = fr[bound]
-    roof = {"kernel": dom, "bound": bound, "achieved": round(ach, 1), "peak": round(peak, 1),
-            "unit": unit, "frac": round(ach / peak, 3),
-            "traffic": traffic_for(dom, args.workload),
-            # what the counters say binds it: the share of SIMD cycles its VALU
-            # and its matrix cores are busy (rocprofv3, committed summary)
-            "issue": issue_for(dom, args.workload),
-            "algorithmic_bytes_per_launch": int(main_by[dom]),
-            "other_bounds": {k: {"achieved": round(v[0], 1), "peak": round(v[1], 1), "unit": v[2],
-                                 "frac": round(v[0] / v[1], 3)} for k, v in fr.items() if k != bound}}
+    by, ops, alu = algorithmic(main_cfg, main_counts)
+    # the dominant kernel: the one with the largest share of the timed step
+    dom = max(pk_main, key=pk_main.get)
+    roof = roofline(dom, by, ops, alu, pk_main, args.workload, main_cfg, main_counts, ms_main)
 
     cpu = None
     if not args.no_cpu_baseline:
         threads = min(16, os.cpu_count() or 1)
         print(f"[bench] cpu baseline on {threads} threads", file=sys.stderr, flush=True)
         cpu = run_cpu_baseline(main_layer, threads, args.cpu_rows)
-        if layer_2k is not None:
+        if "2k" in built and built["2k"][1] is not None:
             # the same chain on one core, at 2,048 tokens
             print("[bench] cpu baseline on one core, 2k layer", file=sys.stderr, flush=True)
-            cpu["one_core_2k"] = run_cpu_baseline(layer_2k, 1, args.cpu_rows_one_core)
+            cpu["one_core_2k"] = run_cpu_baseline(built["2k"][1], 1, args.cpu_rows_one_core)
         cpu["host"] = host_cpu()
+    for v in built.values():
+        v[2].close()
 
+    useful_main = ops["expert_gate_up"] + ops["expert_down"]
     line = {
         "metric": METRIC,
-        "value": m["tops"],
+        "value": round(useful_main / (ms_main * 1e-3) / 1e12, 1),
         "unit": "effective int8 TOPS",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": m["ms_per_layer"],
+        "ms_per_step": round(ms_main, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -384,10 +481,14 @@ def main():
                                f"{main_cfg.routing}, gate/up {'Q2_0' if main_cfg.gu_type == 1 else 'NL4'}, down "
                                f"{'Q2_0' if main_cfg.down_type == 1 else 'NL4'}",
                    "tokens": main_cfg.tokens, "rows": main_cfg.rows, "chunk_rows": args.chunk_rows},
-        "per_kernel_ms": m["per_kernel_ms"],
+        "per_kernel_ms": {k: round(v, 4) for k, v in pk_main.items()},
         "hbm_floor_ms": m["hbm_floor_ms"],
+        "timing": {"value": f"{args.steps} steps between two synchronizations after {args.warmup} "
+                            f"warm-up steps of every layer",
+                   "layers": f"median of {args.rounds} interleaved rounds (fused, four-launch and "
+                             f"with-combine forms of every layer)"},
         "layers": {k: {kk: v[kk] for kk in ("ms_per_layer", "tops", "per_kernel_ms", "hbm_floor_ms",
-                                            "four_launch", "with_combine", "plan")}
+                                            "layer_hbm_frac", "four_launch", "with_combine", "plan")}
                    for k, v in results.items()},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -170,6 +170,10 @@ size_t moe_plan_device_bytes(int tokens, int topk, int n_expert, int chunk_rows)
  * Sorted rows: expert e owns rows [off[e], off[e+1]); inside an expert the
  * rows keep ascending t*topk+k order.  Chunks are (expert, first row, rows),
  * experts by descending row count, ties by ascending expert id.
+ * MOE_EINVAL if a product launch over the plan would exceed one HIP grid
+ * (2^32 - 1 threads: 8 workgroups of 256 threads per item of the longest XCD
+ * list, an item being one chunk against 256 weight rows, or 128 j's of the
+ * fused gate/up).
  * On success *out receives the plan; on error *out is left NULL. */
 int moe_prefill_plan(const int32_t *ids_host, int tokens, int topk, int n_expert,
                      int chunk_rows, const moe_weights *w_gu, const moe_weights *w_down,
@@ -183,7 +187,10 @@ int moe_prefill_plan(const int32_t *ids_host, int tokens, int topk, int n_expert
  *              enqueued on `stream` (it must stay valid until they ran).
  *   plan_dev   required.  Every section the kernels read holds the same bytes
  *              as a host-built plan of the same ids.
- *   n_expert   at most 2048, and tokens*topk below 2^29 (MOE_EINVAL beyond).
+ *   n_expert   at most 2048, and tokens*topk below 2^29 (MOE_EINVAL beyond;
+ *              also when the launches' grid bound below exceeds one HIP grid,
+ *              as for moe_prefill_plan -- e.g. chunk_rows 1 with 32K tokens
+ *              at top-10).
  * Nothing is read back: the call enqueues a host-to-device copy of the two
  * weight offset tables and four small integer launches (per tile of ids, its
  * rows per expert, which also clears the chunk table; per expert, a prefix
@@ -261,12 +268,15 @@ int expert_down(const moe_plan *plan, const void *hq, float *dm, void *stream);
  * evaluated in fp32 as one fmaf per term, k ascending, starting from 0.
  * dm: device fp32 [tokens*topk x hidden] as expert_down writes it; w: device
  * fp32 [tokens x topk] routing weights; out: device fp32 [tokens x hidden];
- * all 16-byte aligned.  MOE_EINVAL if tokens * ceil(hidden/1024) * 256
- * exceeds 2^32 - 1 (the launch's thread count). */
+ * all 16-byte aligned.  One thread per four outputs: MOE_EINVAL if
+ * tokens * hidden / 4 exceeds 2^32 - 1 (the launch's thread count). */
 int moe_combine(const moe_plan *plan, const float *dm, const float *w, float *out, void *stream);
 
 /* Test export: the exact int32 dots of every (sorted row, output, 32-value
- * block) of one product, computed by the same kernel path as the product.
+ * block) of one product, computed by the product kernels' templates in a dots
+ * mode (for Q2_0 the matrix-core kernel decodes every scale as 1, so its
+ * matrix unit returns the dot itself; the small-chunk kernel returns its
+ * int8 dot products), each dot stored as it leaves the matrix or dot unit.
  * product 0 = gate/up (act = xq), 1 = down (act = hq).  Rows
  * [row_begin, row_begin+n_rows) of the sorted order; dots: device int32
  * [n_rows x out_rows x cols/32], 16-byte aligned. */

@@ -20,7 +20,11 @@ constexpr int kSmallActBytes = 32768; // its LDS for the chunk's q8_1 rows
 // latency (about 47 us for gate/up at 8,192 lognormal tokens) where a few
 // more items in the product launch cost next to nothing.
 constexpr int kSmallMinChunks = 96;
-constexpr uint32_t kMagicBits = 0x4B400000u;  // 1.5 * 2^23 as binary32
+// Threads per workgroup of both product kernels; a launch takes kXcds
+// workgroups per item of the longest XCD list, and HIP caps a launch at
+// 2^32 - 1 threads.
+constexpr int kProductThreads = 256;
+constexpr long long kMaxLaunchThreads = 0xFFFFFFFFLL;
 
 constexpr size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
 

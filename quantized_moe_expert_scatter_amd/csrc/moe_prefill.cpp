@@ -29,8 +29,8 @@ struct moe_plan {
     std::vector<int32_t> counts, offsets, perm, inv, chunks, dev_chunks;
     int32_t xcd_tab[kXcdRows * kXcds] = {};
     int n_chunks = 0;
-    int max_xcd_chunks = 0;
-    int max_large[2] = {0, 0}, max_small[2] = {0, 0};   // per product: longest list of each view
+    long long max_xcd_chunks = 0;
+    long long max_large[2] = {0, 0}, max_small[2] = {0, 0};   // per product: longest list of each view
     bool device_built = false;   // sorted maps and chunk lists built on the device
     void *plan_dev = nullptr;
     PlanLayout layout{};
@@ -125,6 +125,20 @@ PlanPtr new_plan(int tokens, int topk, int n_expert, int chunk_rows, const moe_w
     p->dn.codebook = p->dn_codebook;
     p->layout = plan_layout(tokens, topk, n_expert, chunk_rows);
     return p;
+}
+
+// Every product launch over the plan fits one HIP grid: the longest list of
+// each product's two views times that product's N tiles (the fused gate/up
+// takes 128-j tiles), kXcds workgroups of kProductThreads threads per item.
+bool grids_fit(const moe_plan *p) {
+    const long long gu_tiles = std::max<long long>((2LL * p->n_ff + kTileRows - 1) / kTileRows,
+                                                   (p->n_ff + kTileRows / 2 - 1) / (kTileRows / 2));
+    const long long tiles[2] = {gu_tiles, (p->hidden + kTileRows - 1) / kTileRows};
+    for (int q = 0; q < 2; ++q) {
+        const long long items = std::max(p->max_large[q], p->max_small[q]) * tiles[q];
+        if (items * kXcds * kProductThreads > kMaxLaunchThreads) return false;
+    }
+    return true;
 }
 
 // Experts largest first, ties by lower id.
@@ -387,15 +401,16 @@ static int moe_prefill_plan_impl(const int32_t *ids, int tokens, int topk, int n
                 p->xcd_tab[(kXcdLarge + 4 * q + 1) * kXcds + x] = large[q][x];
                 p->xcd_tab[(kXcdSmall + 4 * q) * kXcds + x] = start + large[q][x];
                 p->xcd_tab[(kXcdSmall + 4 * q + 1) * kXcds + x] = cnt[x] - large[q][x];
-                p->max_large[q] = std::max(p->max_large[q], large[q][x]);
-                p->max_small[q] = std::max(p->max_small[q], cnt[x] - large[q][x]);
+                p->max_large[q] = std::max<long long>(p->max_large[q], large[q][x]);
+                p->max_small[q] = std::max<long long>(p->max_small[q], cnt[x] - large[q][x]);
             }
             start += cnt[x];
-            p->max_xcd_chunks = std::max(p->max_xcd_chunks, cnt[x]);
+            p->max_xcd_chunks = std::max<long long>(p->max_xcd_chunks, cnt[x]);
             p->dev_chunks.insert(p->dev_chunks.end(), lists[x].begin(), lists[x].end());
         }
     }
 
+    if (!grids_fit(p.get())) return MOE_EINVAL;
     if (plan_dev) {
         p->plan_dev = plan_dev;
         // the sections after dn_off are the device-built plan's own
@@ -446,6 +461,7 @@ static int moe_prefill_plan_device_impl(const int32_t *ids_dev, int tokens, int 
     p->n_chunks = -1;
     p->max_xcd_chunks = max_chunks(p->rows, n_expert, chunk_rows);
     for (int q = 0; q < 2; ++q) p->max_large[q] = p->max_small[q] = p->max_xcd_chunks;
+    if (!grids_fit(p.get())) return MOE_EINVAL;
     // the two weight offset tables go up from the host, the rest is built there
     st = upload(p.get(), L.gu_off, L.counts, stream,
                 [&](uint8_t *s) {
@@ -563,7 +579,7 @@ static ProductArgs product_args(const moe_plan *p, int product, const void *act)
     a.cols = w.cols;
     a.out_rows = w.rows;
     a.n_tiles = (w.rows + kTileRows - 1) / kTileRows;
-    a.max_items = p->max_xcd_chunks * a.n_tiles;
+    a.max_items = int(p->max_xcd_chunks * a.n_tiles);     // fits: grids_fit at plan time
     if (a.wtype == MOE_W_NL4) std::memcpy(a.codebook, product == 0 ? p->gu_codebook : p->dn_codebook, 16);
     a.small_rows = small_rows_for(w.cols);
     return a;
@@ -574,9 +590,9 @@ static ProductArgs product_args(const moe_plan *p, int product, const void *act)
 // a launch with no item is skipped.
 static hipError_t launch_products(const moe_plan *p, int product, ProductArgs a, hipStream_t stream) {
     hipError_t e = hipSuccess;
-    a.max_items = p->max_small[product] * a.n_tiles;
+    a.max_items = int(p->max_small[product] * a.n_tiles);
     if (a.max_items > 0) e = launch_expert_small(a, stream);
-    a.max_items = p->max_large[product] * a.n_tiles;
+    a.max_items = int(p->max_large[product] * a.n_tiles);
     if (e == hipSuccess && a.max_items > 0) e = launch_expert_product(a, stream);
     return e;
 }
@@ -632,8 +648,8 @@ int moe_combine(const moe_plan *p, const float *dm, const float *w, float *out, 
     if (p->rows == 0) return MOE_OK;
     if (!dm || !w || !out) return MOE_EINVAL;
     if (!aligned16(dm) || !aligned16(w) || !aligned16(out)) return MOE_EALIGN;
-    // one workgroup of 256 threads per 1024 outputs of a token
-    const uint64_t threads = uint64_t(p->tokens) * uint64_t((p->hidden + 1023) / 1024) * 256u;
+    // one thread per float4 of the flat (token, float4) range
+    const uint64_t threads = uint64_t(p->tokens) * uint64_t(p->hidden / 4);
     if (threads > 0xFFFFFFFFull) return MOE_EINVAL;
     return hip_status(launch_combine(dm, w, p->tokens, p->topk, p->hidden, out,
                                      static_cast<hipStream_t>(stream)));

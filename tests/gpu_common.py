@@ -9,8 +9,14 @@ from quantized_moe_expert_scatter_amd import workloads as wl
 from quantized_moe_expert_scatter_amd.layer import DeviceLayer
 
 
-def device_layer(L: wl.Layer, chunk_rows: int = 64) -> DeviceLayer:
-    return DeviceLayer(L.x, L.ids, L.w_gu, L.w_down, chunk_rows=chunk_rows, route_w=L.route_w)
+# guard bytes on each side of every output buffer of a test layer; a layer's
+# close() fails if a kernel wrote into them
+GUARD = 4096
+
+
+def device_layer(L: wl.Layer, chunk_rows: int = 64, **kw) -> DeviceLayer:
+    return DeviceLayer(L.x, L.ids, L.w_gu, L.w_down, chunk_rows=chunk_rows, route_w=L.route_w,
+                       guard=GUARD, **kw)
 
 
 def w_tuple(w: wl.ExpertWeights):
@@ -34,6 +40,27 @@ def oracle_rows(L: wl.Layer, pl: oracle.Plan, rows: np.ndarray, n_threads: int =
 def flip_rows(hq_a: np.ndarray, hq_b: np.ndarray) -> np.ndarray:
     """Rows whose q8_1 bytes differ (an int8 rounding of H fell the other way)."""
     return np.nonzero(np.any(hq_a != hq_b, axis=1))[0]
+
+
+def check_flips(hq_gpu: np.ndarray, hq_ref: np.ndarray, n_ff: int, max_rows: int) -> np.ndarray:
+    """The rows whose H bytes differ, each checked to be an int8 rounding of H
+    that fell the other way: in every differing block each q moves by at most
+    one, the block sum moves by the sum of those moves, and d is equal or one
+    ulp away (the block's largest |h| itself rounded differently).  At most
+    max_rows rows may differ.  Returns the differing rows."""
+    rows = flip_rows(hq_gpu, hq_ref)
+    assert rows.size <= max_rows, f"{rows.size} rows with H bytes differing (bound {max_rows})"
+    if rows.size:
+        q_g, d_g, s_g = oracle.unpack_q8_1(hq_gpu[rows], n_ff)
+        q_o, d_o, s_o = oracle.unpack_q8_1(hq_ref[rows], n_ff)
+        dq = q_g.astype(np.int64) - q_o.astype(np.int64)
+        assert np.abs(dq).max() <= 1, "an H value moved by more than one int8 step"
+        nb = n_ff // 32
+        assert np.array_equal(s_g.astype(np.int64) - s_o.astype(np.int64),
+                              dq.reshape(rows.size, nb, 32).sum(axis=2)), "block sums inconsistent"
+        assert np.all(np.abs(d_g.astype(np.float64) - d_o) <= np.spacing(np.abs(d_o))), \
+            "block scale moved by more than one ulp"
+    return rows
 
 
 def row_rel(a: np.ndarray, ref: np.ndarray) -> np.ndarray:

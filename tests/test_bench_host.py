@@ -63,3 +63,27 @@ def test_counter_records_apply_only_to_their_source(tmp_path, monkeypatch):
     assert bench.traffic_for("k", "other") is None and bench.issue_for("k", "other") is None
     src.write_text("// kernel, changed\n")
     assert bench.traffic_for("k", "w") is None and bench.issue_for("k", "w") is None
+
+
+def test_layer_bytes_and_roofline_fields():
+    """The layer's algorithmic bytes at the 16,384-token shape (every expert
+    touched) are the survey's 5,541.7 MB: per (token, expert) row 28,480 B,
+    per token 10,240 B, per expert 1,382,400 B of Q2_0 weights; the dominant
+    kernel is placed against the int8 matrix-core peak and HBM."""
+    import numpy as np
+    sys.path.insert(0, ROOT)
+    import bench
+    from quantized_moe_expert_scatter_amd import workloads as wl
+    cfg = wl.CONFIGS["16k"]
+    counts = np.full(cfg.n_expert, cfg.rows // cfg.n_expert, np.int64)
+    method, path = bench.layer_bytes(cfg, counts)
+    assert method == cfg.rows * 28480 + cfg.tokens * 10240 + cfg.n_expert * 1382400
+    assert abs(method / 1e6 - 5541.7) < 0.1
+    assert path == method - cfg.rows * 2 * 8 * cfg.n_ff          # GU is never stored
+    by, ops, alu = bench.algorithmic(cfg, counts)
+    pk = {"quantize_scatter": 0.13, "expert_gate_up_swiglu_q8": 1.5, "expert_down": 0.95}
+    r = bench.roofline("expert_gate_up_swiglu_q8", by, ops, alu, pk, "none", cfg, counts, 2.58)
+    assert r["bound"] == "mfma" and r["peak"] == 5000.0
+    assert abs(r["achieved"] - ops["expert_gate_up_swiglu_q8"] / 1.5e-3 / 1e12) < 0.1
+    assert set(r["other_bounds"]) == {"hbm", "mfma_fp16", "alu"}
+    assert abs(r["layer_hbm"]["frac"] - method / 2.58e-3 / 8e12) < 1e-3

@@ -15,6 +15,7 @@ import torch
 from quantized_moe_expert_scatter_amd import _lib
 from quantized_moe_expert_scatter_amd import workloads as wl
 from quantized_moe_expert_scatter_amd.layer import DeviceLayer
+from tests.gpu_common import GUARD
 
 pytestmark = pytest.mark.gpu
 
@@ -102,7 +103,7 @@ def test_device_plan_runs_the_same_chain():
         outs = []
         for dev in (False, True):
             D = DeviceLayer(L.x, L.ids, L.w_gu, L.w_down, chunk_rows=128, route_w=L.route_w,
-                            device_plan=dev)
+                            device_plan=dev, guard=GUARD)
             D.run_fused()
             D.combine()
             torch.cuda.synchronize()
@@ -120,7 +121,8 @@ def test_device_plan_reports_ids_out_of_range():
     ids = L.ids.copy()
     ids[3, 1] = 8
     ids[17, 0] = -5
-    D = DeviceLayer(L.x, ids, L.w_gu, L.w_down, chunk_rows=64, route_w=L.route_w, device_plan=True)
+    D = DeviceLayer(L.x, ids, L.w_gu, L.w_down, chunk_rows=64, route_w=L.route_w, device_plan=True,
+                    guard=GUARD)
     with pytest.raises(_lib.MoeError) as e:
         D.plan.query()
     assert e.value.status == -1
@@ -131,7 +133,7 @@ def test_device_plan_reports_ids_out_of_range():
     # host plan of the valid ids (their rows sit elsewhere, the values do not move)
     ok = np.setdiff1d(np.arange(cfg.tokens), [3, 17])
     good = L.ids.copy()
-    H = DeviceLayer(L.x, good, L.w_gu, L.w_down, chunk_rows=64, route_w=L.route_w)
+    H = DeviceLayer(L.x, good, L.w_gu, L.w_down, chunk_rows=64, route_w=L.route_w, guard=GUARD)
     H.run_fused()
     H.combine()
     torch.cuda.synchronize()

@@ -2,8 +2,10 @@
 
 Bars (the contract of the prefill routed-expert product):
   * q8_1 bytes (d, s, q of every block) bit-exact: Xq from quantize_scatter,
-    Hq from swiglu_q8 (except blocks whose H value differs by the two
-    sides' exp, counted and bounded);
+    Hq from swiglu_q8 (except rows where e^-g lies next to a binary32
+    rounding boundary, so that one side's int8 rounding of H falls the other
+    way: at most 1 % of the rows, each checked to differ by such roundings
+    only);
   * int32 block dots bit-exact (moe_debug_block_dots);
   * expert outputs: rel RMS <= 1e-5 over rows without an H flip, rel <= 1e-2
     on flip rows.  The kernels follow the oracle's epilogue operation for
@@ -21,8 +23,8 @@ from oracle import oracle
 from quantized_moe_expert_scatter_amd import _lib
 from quantized_moe_expert_scatter_amd import workloads as wl
 from quantized_moe_expert_scatter_amd.layer import DeviceLayer
-from tests.gpu_common import (check_expert_outputs, device_layer, flip_rows, oracle_rows,
-                              rel_rms, w_tuple)
+from tests.gpu_common import (GUARD, check_expert_outputs, check_flips, device_layer, flip_rows,
+                              oracle_rows, rel_rms, w_tuple)
 
 pytestmark = pytest.mark.gpu
 
@@ -84,9 +86,8 @@ def _chain_every_element(name, chunk_rows):
     assert np.array_equal(gu.view(np.uint32), ref.gu.view(np.uint32)), \
         f"GU bits: rel RMS {rel_rms(gu, ref.gu):.3e}"
     hq = D.hq_host()
-    flips = flip_rows(hq, ref.hq)
+    flips = check_flips(hq, ref.hq, L.cfg.n_ff, max(2, hq.shape[0] // 100))
     _say("H flip rows", flips.size, "of", hq.shape[0])
-    assert flips.size <= max(2, hq.shape[0] // 100)
     dm = D.dm_host()
     check_expert_outputs(dm, ref.dm, ref.plan.perm[flips], name)
     D.close()
@@ -128,13 +129,10 @@ def test_swiglu_q8_and_down_alone_on_oracle_inputs(name):
     D.swiglu_q8()
     torch.cuda.synchronize()
     hq = D.hq_host()
-    diff_rows = flip_rows(hq, ref.hq)
+    # both sides round e^-g once to binary32 from a binary64 exponential: the
+    # bytes can differ only where e^-g lies next to a binary32 rounding boundary
+    diff_rows = check_flips(hq, ref.hq, cfg.n_ff, max(2, cfg.rows // 100))
     _say("rows whose H bytes differ:", diff_rows.size, "of", cfg.rows)
-    q_g, d_g, s_g = oracle.unpack_q8_1(hq, cfg.n_ff)
-    q_o, d_o, s_o = oracle.unpack_q8_1(ref.hq, cfg.n_ff)
-    assert np.abs(q_g.astype(int) - q_o.astype(int)).max() <= 1
-    assert np.abs(d_g - d_o).max() <= 2 * np.spacing(np.abs(d_o)).max()
-    assert diff_rows.size <= max(2, cfg.rows // 50)
     hq_dev = torch.from_numpy(ref.hq.reshape(-1).copy()).cuda()
     _lib.expert_down(D.plan, hq_dev, D.dm)
     torch.cuda.synchronize()
@@ -175,7 +173,8 @@ def test_deterministic_and_empty():
     # zero tokens: every step is a valid no-op
     E = wl.make_layer(wl.small_config("empty", 1, 256, 128, 8, 2, seed=3))
     from quantized_moe_expert_scatter_amd.layer import DeviceLayer
-    Z = DeviceLayer(np.zeros((0, 256), np.float32), np.zeros((0, 2), np.int32), E.w_gu, E.w_down)
+    Z = DeviceLayer(np.zeros((0, 256), np.float32), np.zeros((0, 2), np.int32), E.w_gu, E.w_down,
+                    guard=GUARD)
     Z.run()
     torch.cuda.synchronize()
     Z.close()
@@ -196,7 +195,7 @@ def test_zero_and_huge_token_rows():
     rows3 = np.nonzero(ref.plan.perm // cfg.topk == 3)[0]
     assert np.all(D.xq_host()[rows3] == 0)
     assert np.all(D.dm_host()[ref.plan.perm[rows3]] == 0.0)
-    flips = flip_rows(D.hq_host(), ref.hq)
+    flips = check_flips(D.hq_host(), ref.hq, cfg.n_ff, 2)
     check_expert_outputs(D.dm_host(), ref.dm, ref.plan.perm[flips], "edge")
     D.close()
 
@@ -258,13 +257,13 @@ def test_interleaved_gate_up_rows(name):
     ref = oracle.layer(L.x, L.ids, cfg.n_expert, cfg.n_ff, w_tuple(Li), w_tuple(L.w_down),
                        n_threads=8, gu_interleaved=True)
     A = device_layer(L)
-    B = DeviceLayer(L.x, L.ids, Li, L.w_down, chunk_rows=64, route_w=L.route_w, gu_interleaved=True)
+    B = DeviceLayer(L.x, L.ids, Li, L.w_down, chunk_rows=64, route_w=L.route_w, gu_interleaved=True,
+                    guard=GUARD)
     for D in (A, B):
         D.run_fused()
     torch.cuda.synchronize()
     assert torch.equal(A.hq, B.hq) and torch.equal(A.dm.view(torch.int32), B.dm.view(torch.int32))
-    flips = flip_rows(B.hq_host(), ref.hq)
-    assert flips.size <= max(2, cfg.rows // 100)
+    flips = check_flips(B.hq_host(), ref.hq, cfg.n_ff, max(2, cfg.rows // 100))
     check_expert_outputs(B.dm_host(), ref.dm, ref.plan.perm[flips], name)
     A.close()
     B.close()
@@ -312,7 +311,7 @@ def _sampled_rows(cfg):
     assert np.array_equal(gu_dev.view(np.uint32), gu.view(np.uint32)), \
         f"GU bits: rel RMS {rel_rms(gu_dev, gu):.3e}"
     hq_dev = D.hq_host()[rows]
-    flips = flip_rows(hq_dev, hq)
+    flips = check_flips(hq_dev, hq, cfg.n_ff, max(2, rows.size // 100))
     _say("H flip rows in sample", flips.size)
     dm_dev = D.dm_host()[pl.perm[rows]]
     check_expert_outputs(dm_dev, dm, flips, name)
