@@ -207,6 +207,28 @@ int moe_prefill_plan_device(const int32_t *ids_dev, int tokens, int topk, int n_
                             int chunk_rows, const moe_weights *w_gu, const moe_weights *w_down,
                             void *plan_dev, size_t plan_dev_bytes, void *stream, moe_plan **out);
 
+/* moe_prefill_plan_device for callers that cannot allocate device memory or
+ * pass a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the plan is built in the library's own
+ * workspace, a 4 MiB array of device memory that each GPU the library runs on
+ * holds until the process ends.  The call allocates nothing (no hipMalloc,
+ * hipHostMalloc, event or host heap memory) and copies nothing from the host:
+ * the weight offset tables are written on the device, so every expert of
+ * w_gu and of w_down must sit at a constant stride from the first
+ * (offset[e] = offset[0] + e * stride; stride 0 shares one matrix), else
+ * MOE_EINVAL.
+ * Arguments and checks as moe_prefill_plan_device, without plan_dev; the
+ * plan's moe_plan_device_bytes(tokens, topk, n_expert, chunk_rows) must be at
+ * most 4 MiB (MOE_ESIZE beyond: about 180,000 rows at 512 experts).
+ * Every plan built this way on a device shares that device's workspace and
+ * one host object: *out stays valid until the next call of this function on
+ * the same device, which overwrites it (finish the steps over one plan before
+ * building the next; calls that overlap on one device race).  moe_plan_destroy
+ * on it does nothing.  moe_plan_query waits for `stream`. */
+int moe_prefill_plan_device_noalloc(const int32_t *ids_dev, int tokens, int topk, int n_expert,
+                                    int chunk_rows, const moe_weights *w_gu,
+                                    const moe_weights *w_down, void *stream, moe_plan **out);
+
 /* Host view of a plan, for inspection and tests: any pointer may be NULL.
  * For a device-built plan it waits for the plan's kernels and reads the plan
  * back (MOE_EINVAL if a routing id was out of range).

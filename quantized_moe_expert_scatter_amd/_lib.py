@@ -25,7 +25,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EALIGN", -3: "MOE_EFORMAT",
 
 # every symbol include/moe_prefill.h declares
 EXPORTS = ["moe_q8_1_bytes", "moe_weight_bytes", "moe_weights_pack", "moe_plan_device_bytes",
-           "moe_prefill_plan", "moe_prefill_plan_device",
+           "moe_prefill_plan", "moe_prefill_plan_device", "moe_prefill_plan_device_noalloc",
            "moe_plan_query", "moe_plan_destroy", "quantize_scatter", "expert_gate_up",
            "swiglu_q8", "expert_gate_up_swiglu_q8", "expert_down", "moe_combine",
            "moe_debug_block_dots",
@@ -70,6 +70,9 @@ def lib() -> ctypes.CDLL:
         L.moe_prefill_plan.restype = I
         L.moe_prefill_plan_device.argtypes = L.moe_prefill_plan.argtypes
         L.moe_prefill_plan_device.restype = I
+        L.moe_prefill_plan_device_noalloc.argtypes = [P, I, I, I, I, ctypes.POINTER(moe_weights),
+                                                      ctypes.POINTER(moe_weights), P, ctypes.POINTER(P)]
+        L.moe_prefill_plan_device_noalloc.restype = I
         L.moe_plan_query.argtypes = [P, ctypes.POINTER(I), ctypes.POINTER(I), P, P, P, P]
         L.moe_plan_query.restype = I
         L.moe_plan_destroy.argtypes = [P]
@@ -218,6 +221,19 @@ def moe_prefill_plan_device(ids_dev, tokens: int, topk: int, n_expert: int, chun
                                        _stream(stream), ctypes.byref(h))
     _check(st, "moe_prefill_plan_device")
     return Plan(h.value, workspace, tokens, topk, n_expert, keep=(w_gu, w_down, ids_dev))
+
+
+def moe_prefill_plan_device_noalloc(ids_dev, tokens: int, topk: int, n_expert: int, chunk_rows: int,
+                                    w_gu: Weights, w_down: Weights, stream=None) -> Plan:
+    """The device plan in the library's own per-device workspace: valid until
+    the next such call on the device (ids_dev is kept alive with the plan)."""
+    h = ctypes.c_void_p()
+    st = lib().moe_prefill_plan_device_noalloc(_ptr(ids_dev) if tokens else None, tokens, topk, n_expert,
+                                               chunk_rows, ctypes.byref(w_gu.struct),
+                                               ctypes.byref(w_down.struct), _stream(stream),
+                                               ctypes.byref(h))
+    _check(st, "moe_prefill_plan_device_noalloc")
+    return Plan(h.value, None, tokens, topk, n_expert, keep=(w_gu, w_down, ids_dev))
 
 
 # ------------------------------------------------------------------ steps

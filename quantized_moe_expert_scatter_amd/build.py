@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_prefill.so")
 SOURCES = ["moe_prefill.cpp", "quant_kernels.hip", "expert_kernels.hip", "weight_pack.hip",
-           "combine_kernels.hip", "plan_kernels.hip", "expert_small_kernels.hip"]
+           "combine_kernels.hip", "plan_kernels.hip", "expert_small_kernels.hip", "plan_scratch.hip"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

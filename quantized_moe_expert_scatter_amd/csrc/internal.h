@@ -156,6 +156,15 @@ hipError_t launch_device_plan(const int32_t *ids, int rows, int n_expert, int ch
 // the grid is tokens * ceil(hidden / 1024) workgroups of 256 threads.
 hipError_t launch_combine(const float *dm, const float *w, int tokens, int topk, int hidden,
                           float *out, hipStream_t stream);
+// The library's own plan workspace on each device (plan_scratch.hip), for
+// plans built without caller memory: its size, and its device address on the
+// current device (looked up once per device).
+constexpr size_t kScratchBytes = size_t(4) << 20;
+hipError_t scratch_workspace(void **ptr);
+// Weight offset tables of experts at a constant stride, written on the device.
+hipError_t launch_stride_offsets(uint64_t *gu_off, uint64_t gu_first, uint64_t gu_stride,
+                                 uint64_t *dn_off, uint64_t dn_first, uint64_t dn_stride,
+                                 int n_expert, hipStream_t stream);
 // Packs n_expert matrices of rows x blocks_per_row blocks into the tiled
 // layout; expert e's planes start at src/dst + e * expert_stride.  half > 0:
 // the source rows alternate gate/up (2j gate j, 2j+1 up j, j < half) and the

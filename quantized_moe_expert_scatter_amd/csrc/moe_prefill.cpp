@@ -32,6 +32,8 @@ struct moe_plan {
     long long max_xcd_chunks = 0;
     long long max_large[2] = {0, 0}, max_small[2] = {0, 0};   // per product: longest list of each view
     bool device_built = false;   // sorted maps and chunk lists built on the device
+    bool in_scratch = false;     // built in the library's per-device workspace: not freed
+    hipStream_t stream = nullptr;  // the stream a plan without an upload event was built on
     void *plan_dev = nullptr;
     PlanLayout layout{};
     void *staging = nullptr;     // pinned, from the staging pool
@@ -487,6 +489,79 @@ int moe_prefill_plan_device(const int32_t *ids_dev, int tokens, int topk, int n_
     });
 }
 
+// The experts of w at a constant stride: offset[e] = offset[0] + e * stride
+// (stride 0: one shared matrix).
+static bool strided(const moe_weights *w, uint64_t *first, uint64_t *stride) {
+    *first = w->offset[0];
+    *stride = w->n_expert > 1 ? w->offset[1] - w->offset[0] : 0;
+    for (int e = 1; e < w->n_expert; ++e)
+        if (w->offset[e] < w->offset[0] || w->offset[e] - w->offset[0] != uint64_t(e) * *stride)
+            return false;
+    return true;
+}
+
+// One plan object per device for plans in the library's workspace (never
+// freed; the next such plan on the device takes it over).
+static moe_plan g_scratch_plans[64];
+
+static int moe_prefill_plan_device_noalloc_impl(const int32_t *ids_dev, int tokens, int topk,
+                                                int n_expert, int chunk_rows,
+                                                const moe_weights *w_gu, const moe_weights *w_down,
+                                                void *stream, moe_plan **out) {
+    if (!out) return MOE_EINVAL;
+    *out = nullptr;
+    int st = check_plan_args(tokens, topk, n_expert, chunk_rows, w_gu, w_down);
+    if (st) return st;
+    if ((tokens > 0 && !ids_dev) || n_expert > kPlanMaxExperts) return MOE_EINVAL;
+    if ((long long)tokens * topk >= (1LL << 29)) return MOE_EINVAL;
+    if (ids_dev && !aligned16(ids_dev)) return MOE_EALIGN;
+    uint64_t gu_first, gu_stride, dn_first, dn_stride;
+    if (!strided(w_gu, &gu_first, &gu_stride) || !strided(w_down, &dn_first, &dn_stride))
+        return MOE_EINVAL;
+    const PlanLayout L = plan_layout(tokens, topk, n_expert, chunk_rows);
+    if (L.total > kScratchBytes) return MOE_ESIZE;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_EHIP;
+    void *ws = nullptr;
+    if (scratch_workspace(&ws) != hipSuccess) return MOE_EHIP;
+    // the device's plan object: its fields are set here, its containers stay empty
+    moe_plan *p = &g_scratch_plans[dev];
+    p->tokens = tokens; p->topk = topk; p->n_expert = n_expert; p->chunk_rows = chunk_rows;
+    p->rows = tokens * topk; p->hidden = w_gu->cols; p->n_ff = w_gu->rows / 2;
+    p->gu = *w_gu; p->dn = *w_down;
+    p->gu.offset = nullptr; p->dn.offset = nullptr;      // on the device only
+    if (base_type(w_gu->type) == MOE_W_NL4) std::memcpy(p->gu_codebook, w_gu->codebook, 16);
+    if (base_type(w_down->type) == MOE_W_NL4) std::memcpy(p->dn_codebook, w_down->codebook, 16);
+    p->gu.codebook = p->gu_codebook; p->dn.codebook = p->dn_codebook;
+    p->layout = L;
+    p->n_chunks = -1;
+    p->max_xcd_chunks = max_chunks(p->rows, n_expert, chunk_rows);
+    for (int q = 0; q < 2; ++q) p->max_large[q] = p->max_small[q] = p->max_xcd_chunks;
+    p->device_built = true; p->in_scratch = true;
+    p->plan_dev = ws; p->stream = static_cast<hipStream_t>(stream);
+    p->staging = nullptr; p->staging_cap = 0; p->uploaded = nullptr;
+    if (!grids_fit(p)) return MOE_EINVAL;
+    uint8_t *w8 = static_cast<uint8_t *>(ws);
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (launch_stride_offsets(reinterpret_cast<uint64_t *>(w8 + L.gu_off), gu_first, gu_stride,
+                              reinterpret_cast<uint64_t *>(w8 + L.dn_off), dn_first, dn_stride, n_expert,
+                              hs) != hipSuccess ||
+        launch_device_plan(ids_dev, p->rows, n_expert, chunk_rows, small_rows_for(p->hidden),
+                           small_rows_for(p->n_ff), w8, L, hs) != hipSuccess)
+        return MOE_EHIP;
+    *out = p;
+    return MOE_OK;
+}
+
+int moe_prefill_plan_device_noalloc(const int32_t *ids_dev, int tokens, int topk, int n_expert,
+                                    int chunk_rows, const moe_weights *w_gu,
+                                    const moe_weights *w_down, void *stream, moe_plan **out) {
+    return guarded([&] {
+        return moe_prefill_plan_device_noalloc_impl(ids_dev, tokens, topk, n_expert, chunk_rows, w_gu,
+                                                    w_down, stream, out);
+    });
+}
+
 static int moe_plan_query_impl(const moe_plan *p, int *rows, int *n_chunks, int32_t *counts,
                                int32_t *offsets, int32_t *perm, int32_t *chunks) {
     if (!p) return MOE_EINVAL;
@@ -496,7 +571,9 @@ static int moe_plan_query_impl(const moe_plan *p, int *rows, int *n_chunks, int3
         std::vector<int32_t> dc(E + 1), doff(E + 2), dperm(p->rows), status(1);
         const uint8_t *ws = static_cast<const uint8_t *>(p->plan_dev);
         const PlanLayout &L = p->layout;
-        if (hipEventSynchronize(p->uploaded) != hipSuccess ||
+        const hipError_t built = p->uploaded ? hipEventSynchronize(p->uploaded)
+                                             : hipStreamSynchronize(p->stream);
+        if (built != hipSuccess ||
             hipMemcpy(dc.data(), ws + L.counts, dc.size() * 4, hipMemcpyDeviceToHost) != hipSuccess ||
             hipMemcpy(doff.data(), ws + L.offsets, doff.size() * 4, hipMemcpyDeviceToHost) != hipSuccess ||
             hipMemcpy(status.data(), ws + L.aux + 4 * size_t(PlanAux::status(E)), 4,
@@ -532,7 +609,7 @@ int moe_plan_query(const moe_plan *p, int *rows, int *n_chunks, int32_t *counts,
 }
 
 void moe_plan_destroy(moe_plan *p) {
-    if (!p) return;
+    if (!p || p->in_scratch) return;
     if (p->uploaded) {
         (void)hipEventSynchronize(p->uploaded);
         (void)hipEventDestroy(p->uploaded);
