@@ -32,10 +32,10 @@
 //    oracle's.  NL4 codebook entries are exact in fp16 too; there the MFMA
 //    returns the dot itself and the epilogue is fmaf(dx, d * dot, acc) with
 //    the product rounded once, as the oracle rounds it.
-//    (The kernel is bound by VALU issue -- the epilogue FMAs and the weight
-//    decode, four cycles per wave64 instruction -- with the MFMAs largely
-//    hidden under that stream; a 16x16x32 form with the same VALU count per
-//    stage measured the same.)
+//    (The kernel is bound by VALU issue -- the epilogue FMAs, the weight
+//    decode and the activation staging, four cycles per wave64 instruction --
+//    with the MFMAs partly hidden under that stream; a 16x16x32 form with the
+//    same VALU count per stage measured the same.)
 //  * MFMA operands: A = weights (lane l: weight row l%32), B = activations
 //    (lane l: activation row l%32); lane half kq = l/32 holds values
 //    16g + 8kq + p (p < 8) of a 32-value block in the MFMA of half g.  Any
@@ -110,14 +110,19 @@ __device__ __forceinline__ void i8x4_to_f16(uint32_t w, uint32_t &lo, uint32_t &
     hi = as_u32(as_v2h(perm(0x64646464u, u, 0x07030602u)) + bias);
 }
 
-// Q2_0: four 2-bit codes, one per byte of c (values 0..3) -> four fp16
-// weights d*(c-2).  The table holds the four fp16 values {-2d, -d, 0, d}:
-// low bytes in tlo, high bytes in thi, so code c selects byte c and c+4.
-__device__ __forceinline__ void q2_to_f16(uint32_t c, uint32_t thi, uint32_t tlo, uint32_t &h01,
-                                          uint32_t &h23) {
-    const uint32_t c4 = c | 0x04040404u;
-    h01 = perm(thi, tlo, perm(c4, c, 0x05010400u));
-    h23 = perm(thi, tlo, perm(c4, c, 0x07030602u));
+// Q2_0: field J (the codes of values 16J + b) of the four code bytes in
+// `word`, made into four fp16 weights d*(c-2).  The table {-2d, -d, 0, d}
+// keeps its low bytes in tlo and its high bytes in thi: one byte lookup in
+// each gives the four low and the four high bytes, two byte interleaves give
+// the fp16 pairs.
+template <int J>
+__device__ __forceinline__ void q2_decode4(uint32_t word, uint32_t thi, uint32_t tlo, uint32_t &h01,
+                                           uint32_t &h23) {
+    const uint32_t c = (J == 0 ? word : word >> (2 * J)) & 0x03030303u;
+    const uint32_t lo = perm(0u, tlo, c);
+    const uint32_t hi = perm(0u, thi, c);
+    h01 = perm(hi, lo, 0x05010400u);
+    h23 = perm(hi, lo, 0x07030602u);
 }
 
 // NL4: four 4-bit codes (low nibbles of the bytes of c) -> four int8
@@ -161,9 +166,8 @@ template <int WTYPE, int H, int G>
 __device__ __forceinline__ v8h decode_ops(const WRaw &w, uint32_t thi, uint32_t tlo, const uint32_t (&cb)[4]) {
     uint32_t r[4];
     if constexpr (WTYPE == 1) {
-        constexpr int sh = 2 * (2 * H + G);
-        q2_to_f16((w.c0.x >> sh) & 0x03030303u, thi, tlo, r[0], r[1]);
-        q2_to_f16((w.c0.y >> sh) & 0x03030303u, thi, tlo, r[2], r[3]);
+        q2_decode4<2 * H + G>(w.c0.x, thi, tlo, r[0], r[1]);
+        q2_decode4<2 * H + G>(w.c0.y, thi, tlo, r[2], r[3]);
     } else {
         const uint2 c = H == 0 ? w.c0 : w.c1;
         constexpr int sh = 4 * G;
@@ -183,6 +187,15 @@ __device__ __forceinline__ void q2_table(uint32_t hb, uint32_t &thi, uint32_t &t
     const uint32_t neg = pos ^ 0x80008000u;                  // {-d, -2d}
     tlo = perm(neg, pos, 0x000C0406u);
     thi = perm(neg, pos, 0x010C0507u);
+}
+
+// Quarter i of the staging of one activation block: 8 q bytes to fp16 in LDS.
+__device__ __forceinline__ void stage_piece(const ARaw &a, int i, uint8_t *dst) {
+    const uint32_t q[8] = {a.q0.x, a.q0.y, a.q0.z, a.q0.w, a.q1.x, a.q1.y, a.q1.z, a.q1.w};
+    uint4 o;
+    i8x4_to_f16(q[2 * i], o.x, o.y);
+    i8x4_to_f16(q[2 * i + 1], o.z, o.w);
+    *reinterpret_cast<uint4 *>(dst + 16 * i) = o;
 }
 
 // Convert one staged activation block to fp16 and store it in LDS.
@@ -214,15 +227,20 @@ struct Lds {
 
 // One stage (two 32-value blocks h) of Q2_0 outputs, software pipelined as
 // one stream of MFMA pairs n = (h, r, t) (activation tile r, weight tile t):
-// the epilogue of pair n-1 is split between the two MFMAs of pair n, so the
-// vector ALU works on one result while the matrix unit computes the next;
-// each activation operand is read from LDS right after its last use by the
-// previous row tile; the second block's weights are decoded into the
-// registers of the first as soon as those are dead, inside the stream.
-// Scheduling barriers keep that order.
+// each pair issues its two MFMAs back to back, then the whole epilogue of
+// pair n-1, so the vector ALU works on one result while the matrix unit
+// computes the next, and every FMA reads an MFMA result issued eighteen or
+// more instructions earlier (no hazard wait states); each activation operand
+// is read from LDS right after its last use by the previous row tile; the
+// second block's weights are decoded into the registers of the first as soon
+// as those are dead, inside the stream.  The staging of the next stage's
+// activations (four quarters) and the next stage's weight tables (each
+// tile's once its block 1 is decoded) run inside the stream too, ahead of the
+// pairs' FMAs.  Scheduling barriers keep that order.
 template <int NA>
-__device__ __forceinline__ void stage_q2_pipelined(v16f (&acc)[2][NA], const WRaw (&w)[2], const uint32_t (&thi)[2],
-                                                   const uint32_t (&tlo)[2], const uint8_t *arow0,
+__device__ __forceinline__ void stage_q2_pipelined(v16f (&acc)[2][NA], const WRaw (&w)[2], const WRaw (&wn)[2],
+                                                   uint32_t (&thi)[2], uint32_t (&tlo)[2], const ARaw &anext,
+                                                   uint8_t *sdst, float *sdx, const uint8_t *arow0,
                                                    const float *dxrow0) {
     constexpr int NP = 4 * NA;                    // pairs in the stage
     const uint32_t cb[4] = {0u, 0u, 0u, 0u};
@@ -247,31 +265,34 @@ __device__ __forceinline__ void stage_q2_pipelined(v16f (&acc)[2][NA], const WRa
         constexpr bool next = t == 1 && (r + 1 < NA || h == 0);
         constexpr int nh = r + 1 < NA ? h : 1, nr = r + 1 < NA ? r + 1 : 0;
         const uint8_t *nsrc = arow0 + nr * 32 * kARow + 64 * nh;
-        // segment A: first MFMA of the pair, next b0, first half of the previous epilogue
+        // the pair's two MFMAs back to back (the second accumulates onto the
+        // first), the next operands, a quarter of the staging or a table,
+        // then the whole epilogue of the previous pair: its MFMAs issued
+        // eighteen instructions earlier, so the FMAs read finished results
         v16f p = __builtin_amdgcn_mfma_f32_32x32x16_f16(wop[t][0], b0, v16f{}, 0, 0, 0);
-        if constexpr (next) b0 = *reinterpret_cast<const v8h *>(nsrc);
-        if constexpr (n > 0) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[pt][pr][i] = __builtin_fmaf(pdx, prev[i], acc[pt][pr][i]);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, next ? 1 : 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, n > 0 ? 8 : 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        // segment B: second MFMA, next b1 and dx, second half of the previous epilogue
         p = __builtin_amdgcn_mfma_f32_32x32x16_f16(wop[t][1], b1, p, 0, 0, 0);
         const float cdx = dx;
         if constexpr (next) {
+            b0 = *reinterpret_cast<const v8h *>(nsrc);
             b1 = *reinterpret_cast<const v8h *>(nsrc + 32);
             dx = dxrow0[nr * 32 * 2 + nh];
         }
+        static_for<0, 4>([&](auto II) {
+            constexpr int i = decltype(II)::value;
+            constexpr int at = i * NA + 1 < NP - 1 ? i * NA + 1 : NP - 1;
+            if constexpr (at == n) {
+                stage_piece(anext, i, sdst);
+                if constexpr (i == 3) *sdx = anext.d;
+            }
+        });
+        // the next stage's table of tile t, once block 1 of tile t is decoded
+        if constexpr (h == 1 && r == 0) q2_table(wn[t].s, thi[t], tlo[t]);
         if constexpr (n > 0) {
 #pragma unroll
-            for (int i = 8; i < 16; ++i) acc[pt][pr][i] = __builtin_fmaf(pdx, prev[i], acc[pt][pr][i]);
+            for (int i = 0; i < 16; ++i) acc[pt][pr][i] = __builtin_fmaf(pdx, prev[i], acc[pt][pr][i]);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, next ? 2 : 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, n > 0 ? 8 : 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, next ? 3 : 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         // block 1's weights of tile t once block 0's last pair of tile t has issued
         if constexpr (h == 0 && r == NA - 1) {
@@ -291,32 +312,62 @@ constexpr int kOut = 0;     // fp32 outputs
 constexpr int kDots = 1;    // the int32 block dots (test export)
 constexpr int kSwiglu = 2;  // gate/up with swiglu and q8_1 of H in the epilogue
 
+// q8_1 of one lane's 16 values of a 32-value block whose other 16 sit in
+// lane ^ 32: d = max|x| / 127 (the fp32 divide), q = x / d rounded half away
+// from zero and clamped to [-127, 127].  x / d is the correctly rounded
+// binary32 quotient without a divide per value: r = 1/d in binary64 (one
+// divide per block), then x * r rounded to binary64 and that to binary32.
+// That is exact because the quotient of two binary32 values is never a
+// binary32 rounding boundary and lies at least 2^-49 of its size away from
+// one, while x * r is within 2^-52 of it.  The rounding adds +-1/2 in
+// binary64 (exact for |y| <= 127) and truncates.  q bytes are packed four to
+// a word, value i of the lane in byte i % 4 of word i / 4.
+__device__ __forceinline__ void q8_1_half_block(const float (&x)[16], uint32_t (&w)[4], float &d,
+                                                int32_t &sum) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
+    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
+    d = amax / 127.0f;
+    sum = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = 0u;
+    if (d != 0.0f) {
+        const double r = 1.0 / static_cast<double>(d);
+        int32_t q[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float y = static_cast<float>(static_cast<double>(x[i]) * r);
+            const float yc = __builtin_amdgcn_fmed3f(y, -127.0f, 127.0f);
+            const double half = __builtin_copysign(0.5, static_cast<double>(yc));
+            q[i] = static_cast<int32_t>(static_cast<double>(yc) + half);
+            sum += q[i];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t lo = perm(uint32_t(q[4 * k + 1]), uint32_t(q[4 * k]), 0x0C0C0400u);
+            const uint32_t hi = perm(uint32_t(q[4 * k + 3]), uint32_t(q[4 * k + 2]), 0x04000C0Cu);
+            w[k] = lo | hi;
+        }
+    }
+    sum += __shfl_xor(sum, 32);
+}
+
 // Fused epilogue for one activation row: the lane holds gate (tile 0) and up
 // (tile 1) of the same 16 j's, h = silu(g) * u exactly as swiglu_q8 computes
 // it, and the 32-value q8_1 block of h is shared with lane ^ 32.
 __device__ __forceinline__ void swiglu_store_row(const v16f &g, const v16f &u, uint8_t *hrow, int n_ff,
                                                  int jbase, int kq) {
     float h[16];
-    float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const float e = static_cast<float>(exp(-static_cast<double>(g[i])));
         h[i] = g[i] / (1.0f + e) * u[i];
-        amax = __builtin_fmaxf(amax, __builtin_fabsf(h[i]));
     }
-    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
-    const float d = amax / 127.0f;
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    int32_t sum = 0;
-    if (d != 0.0f) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int8_t q = q8_round(h[i], d);
-            sum += q;
-            w[i >> 2] |= uint32_t(uint8_t(q)) << (8 * (i & 3));
-        }
-    }
-    sum += __shfl_xor(sum, 32);
+    uint32_t w[4];
+    float d;
+    int32_t sum;
+    q8_1_half_block(h, w, d, sum);
     // value i of the lane is j = jbase + 8 (i / 4) + 4 kq + i % 4
 #pragma unroll
     for (int q = 0; q < 4; ++q) *reinterpret_cast<uint32_t *>(hrow + jbase + 8 * q + 4 * kq) = w[q];
@@ -471,6 +522,12 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
         __builtin_amdgcn_sched_barrier(0);
     }
     stage_acts(aslot[0], &L.act[0][srow * kARow + 64 * sblk], &L.dx[0][srow][sblk]);
+    // the pipelined Q2_0 stage computes the next stage's weight tables itself
+    uint32_t pthi[2] = {0u, 0u}, ptlo[2] = {0u, 0u};
+    if constexpr (PIPE) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) q2_table(wslot[0][t].s, pthi[t], ptlo[t]);
+    }
     __syncthreads();
 
     auto stage = [&](auto J, int s) {
@@ -484,6 +541,18 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
         // (or before the loop), so it takes the load of stage s + U now
         aslot[j] = aload(s + U);
 
+        if constexpr (PIPE) {
+            if (wave_on && s < n_stages)
+                stage_q2_pipelined<NA>(acc, wslot[j], wslot[jn], pthi, ptlo, aslot[jn],
+                                       &L.act[par ^ 1][srow * kARow + 64 * sblk], &L.dx[par ^ 1][srow][sblk],
+                                       L.act[par] + col * kARow + 16 * kq, &L.dx[par][col][0]);
+            else
+                stage_acts(aslot[jn], &L.act[par ^ 1][srow * kARow + 64 * sblk], &L.dx[par ^ 1][srow][sblk]);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) wslot[j][t] = wload(s + U, t);
+            __syncthreads();
+            return;
+        }
         if (wave_on && s < n_stages) {
             uint32_t thi[2] = {0u, 0u}, tlo[2] = {0u, 0u};
             if constexpr (WTYPE == 1) {
@@ -501,10 +570,7 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
                 __builtin_amdgcn_wave_barrier();
             }
             const uint8_t *abuf = L.act[par];
-            if constexpr (PIPE) {
-                stage_q2_pipelined<NA>(acc, wslot[j], thi, tlo, abuf + col * kARow + 16 * kq,
-                                       &L.dx[par][col][0]);
-            } else static_for<0, 2>([&](auto HH) {
+            static_for<0, 2>([&](auto HH) {
                 constexpr int h = decltype(HH)::value;
                 if (h < nblk) {
                     v8h wop[2][2];
