@@ -69,6 +69,7 @@
 namespace moe {
 
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -136,11 +137,11 @@ __device__ __forceinline__ uint32_t nl4_lookup(uint32_t c, const uint32_t (&cb)[
     return (hi & mask) | (lo & ~mask);
 }
 
-__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+__device__ __forceinline__ _Float16 half_bits(uint32_t h) {
     const uint16_t b = uint16_t(h);
     _Float16 v;
     __builtin_memcpy(&v, &b, 2);
-    return static_cast<float>(v);
+    return v;
 }
 
 // Raw weight bytes of one lane for one stage and one 32-row weight tile:
@@ -222,7 +223,7 @@ __device__ __forceinline__ void static_for(F &&f) {
 struct Lds {
     uint8_t act[2][kMaxRows * kARow];   // staged fp16 activations, double buffered
     float dx[2][kMaxRows][2];           // their block scales (two blocks per stage)
-    float dw[kWaves][2][2][32];         // NL4: block scales of each wave's weight rows
+    _Float16 dw[kWaves][2][2][32];      // NL4: block scales of each wave's weight rows
 };
 
 // One stage (two 32-value blocks h) of Q2_0 outputs, software pipelined as
@@ -431,32 +432,30 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
                     (uint32_t(uint8_t(a.codebook[4 * i + 2])) << 16) |
                     (uint32_t(uint8_t(a.codebook[4 * i + 3])) << 24);
     }
-    // Q2_0 items read the expert's two planes (codes, then scales) through
-    // one buffer descriptor: the lane's offsets stay in registers, the
-    // stage's offset is a scalar.
-    constexpr bool BUF = WTYPE == 1;
+    // Items read the expert's two planes (codes, then scales) through one
+    // buffer descriptor: the lane's offsets stay in registers, the stage's
+    // offset is a scalar, and the descriptor's range keeps every access
+    // inside the expert.  Q2_0: one 64-value block per stage; NL4: two
+    // 32-value blocks (the second one 32 slots on, absent past the end of a
+    // row of odd block count: its bytes are loaded but never used).
     const uint32_t codes_bytes = uint32_t(a.out_rows) * uint32_t(nbw) * 16u;
-    const uint16_t *wscales = reinterpret_cast<const uint16_t *>(wexp + codes_bytes);
     const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
         (void *)uniform_ptr(wexp), 0, __builtin_amdgcn_readfirstlane(int(codes_bytes + codes_bytes / 8u)),
         0x00020000);
     auto wload = [&](int stage, int t) {
         const int s = min(stage, n_stages - 1);
         const int blk = s * (kKS / WB);                      // first block of the stage
-        const bool second = WTYPE == 2 && blk + 1 < nbw;
         WRaw w;
-        if constexpr (BUF) {
-            w.c0 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(wres, coff[t], blk * 512, 0));
+        w.c0 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(wres, coff[t], blk * 512, 0));
+        if constexpr (WTYPE == 1) {
             w.c1 = w.c0;
             w.s = __builtin_amdgcn_raw_buffer_load_b16(wres, 2u * soff[t], int(codes_bytes) + blk * 64, 0);
         } else {
-            const uint8_t *codes = wexp + size_t(blk) * 512;
-            const uint16_t *scales = wscales + 32 * blk;
-            const uint32_t o1 = second ? 32u : 0u;       // the next block of the same 32 rows
-            w.c0 = *reinterpret_cast<const uint2 *>(codes + coff[t]);
-            w.c1 = WTYPE == 1 ? w.c0 : *reinterpret_cast<const uint2 *>(codes + coff[t] + 16u * o1);
-            w.s = WTYPE == 1 ? uint32_t(scales[soff[t]])
-                             : uint32_t(scales[soff[t]]) | (uint32_t(scales[soff[t] + o1]) << 16);
+            const int b1 = min(blk + 1, nbw - 1);            // the next block of the same 32 rows
+            w.c1 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(wres, coff[t], b1 * 512, 0));
+            w.s = uint32_t(__builtin_amdgcn_raw_buffer_load_b16(wres, 2u * soff[t], int(codes_bytes) + blk * 64, 0)) |
+                  (uint32_t(__builtin_amdgcn_raw_buffer_load_b16(wres, 2u * soff[t], int(codes_bytes) + b1 * 64, 0))
+                   << 16);
         }
         return w;
     };
@@ -466,25 +465,18 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
     const int sblk = tid & 1;
     const uint8_t *abase = a.act + size_t(row0) * arb;
     const uint32_t aoff = uint32_t(min(srow, nrows - 1)) * arb;
-    // the chunk's rows through one descriptor (Q2_0 items; a stage holds two
-    // whole blocks, and past the chunk the range check returns zeros), else
-    // through clamped, always in-bounds 64-bit addresses
+    // the chunk's rows through one descriptor (past the chunk the range
+    // check returns zeros; the block after the last of a row of odd block
+    // count reads the row's own scales and sums, staged but never used)
     const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
         (void *)uniform_ptr(abase), 0, __builtin_amdgcn_readfirstlane(int(uint32_t(nrows) * arb)), 0x00020000);
     const uint32_t aq = aoff + 32u * uint32_t(sblk), ad = aoff + uint32_t(cols) + 4u * uint32_t(sblk);
     auto aload = [&](int stage) {
         const int s = min(stage, n_stages - 1);
         ARaw r;
-        if constexpr (BUF) {
-            r.q0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, aq, 64 * s, 0));
-            r.q1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, aq + 16u, 64 * s, 0));
-            r.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ares, ad, 8 * s, 0));
-        } else {
-            const int kb = min(s * 2 + sblk, nb32 - 1);
-            r.q0 = *reinterpret_cast<const uint4 *>(abase + aoff + 32u * kb);
-            r.q1 = *reinterpret_cast<const uint4 *>(abase + aoff + 32u * kb + 16u);
-            r.d = *reinterpret_cast<const float *>(abase + aoff + uint32_t(cols) + 4u * kb);
-        }
+        r.q0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, aq, 64 * s, 0));
+        r.q1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, aq + 16u, 64 * s, 0));
+        r.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ares, ad, 8 * s, 0));
         return r;
     };
 
@@ -563,8 +555,8 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
                 if (kq == 0) {
 #pragma unroll
                     for (int t = 0; t < 2; ++t) {
-                        L.dw[wave][0][t][col] = half_bits_to_float(wslot[j][t].s & 0xFFFFu);
-                        L.dw[wave][1][t][col] = half_bits_to_float(wslot[j][t].s >> 16);
+                        L.dw[wave][0][t][col] = half_bits(wslot[j][t].s & 0xFFFFu);
+                        L.dw[wave][1][t][col] = half_bits(wslot[j][t].s >> 16);
                     }
                 }
                 __builtin_amdgcn_wave_barrier();
@@ -579,13 +571,14 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
                         wop[t][0] = decode_ops<WTYPE, h, 0>(wslot[j][t], thi[t], tlo[t], cb);
                         wop[t][1] = decode_ops<WTYPE, h, 1>(wslot[j][t], thi[t], tlo[t], cb);
                     }
-                    v4f dwv[2][4];
+                    // NL4: the lane's 16 weight-row scales of each tile, binary16
+                    v4h dwv[2][4];
                     if constexpr (WTYPE == 2) {
 #pragma unroll
                         for (int t = 0; t < 2; ++t)
 #pragma unroll
                             for (int q = 0; q < 4; ++q)
-                                dwv[t][q] = *reinterpret_cast<const v4f *>(&L.dw[wave][h][t][8 * q + 4 * kq]);
+                                dwv[t][q] = *reinterpret_cast<const v4h *>(&L.dw[wave][h][t][8 * q + 4 * kq]);
                     }
 #pragma unroll
                     for (int r = 0; r < NA; ++r) {
@@ -611,9 +604,13 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
 #pragma unroll
                                 for (int i = 0; i < 16; ++i) acc[t][r][i] = __builtin_fmaf(dx, p[i], acc[t][r][i]);
                             } else {
+                                // dw * dot rounded once (an fma onto -0 is the plain
+                                // product, signed zeros included), then the epilogue fma
 #pragma unroll
-                                for (int i = 0; i < 16; ++i)
-                                    acc[t][r][i] = __builtin_fmaf(dx, dwv[t][i >> 2][i & 3] * p[i], acc[t][r][i]);
+                                for (int i = 0; i < 16; ++i) {
+                                    const float wd = __builtin_fmaf(static_cast<float>(dwv[t][i >> 2][i & 3]), p[i], -0.0f);
+                                    acc[t][r][i] = __builtin_fmaf(dx, wd, acc[t][r][i]);
+                                }
                             }
                         }
                     }
