@@ -13,7 +13,9 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmoe_prefill.so")
+# MOE_PREFILL_LIB names another build of the same library (the host
+# sanitizer run in tests/sanitize loads an instrumented one)
+LIB_PATH = os.environ.get("MOE_PREFILL_LIB") or os.path.join(HERE, "libmoe_prefill.so")
 
 MOE_W_Q2_0 = 1
 MOE_W_NL4 = 2
