@@ -52,6 +52,9 @@
  *   (row tile, block, row in tile) order for 32-row tiles -- block b of row
  *   32*i + r sits at slot (i * blocks_per_row + b) * 32 + r of its plane, so
  *   the 32 rows of one block are 512 contiguous code bytes and 64 scale bytes.
+ *   Within a Q2_0 block the codes are also reordered: the code of value
+ *   v = 32*h + 16*g + 8*kq + p (h, g, kq < 2, p < 8) sits at bits
+ *   2*g + 4*(p%2) .. +1 of byte 8*kq + 4*h + p/2.  NL4 blocks are unchanged.
  *   Expert outputs are fp32.  The per-32-value epilogue is, for each output,
  *       acc = 0; for each 32-value block b in K order:
  *         acc = fmaf(dx_b, dw_b * (float)dot_b, acc)

@@ -14,11 +14,18 @@
 //    one expert against 256 of that expert's weight rows (the N tile); each of
 //    its 4 wavefronts owns 64 weight rows (two 32-row tiles).
 //  * For each 64-value K stage the workgroup converts the chunk's q8_1 values
-//    to fp16 once and stages them in LDS (double buffered); each wavefront
-//    decodes its own weight blocks straight into MFMA operand registers, so
-//    every weight block is decoded exactly once and never round-trips
-//    through LDS, and every activation operand read from LDS feeds both of
-//    the wave's weight tiles.
+//    to fp16 once and stages them in LDS (double buffered; four lanes read
+//    one row's 64 contiguous bytes, and one conversion per value picks and
+//    packs the signed byte); each wavefront decodes its own weight blocks
+//    straight into MFMA operand registers, so every weight block is decoded
+//    exactly once and never round-trips through LDS, and every activation
+//    operand read from LDS feeds both of the wave's weight tiles.
+//  * Q2_0 decode: the tiled layout keeps, in each byte of a lane's code
+//    word, two codes in the low bits of its nibbles (and two more above
+//    them); after one mask a nibble 00cc read as FP4 (E2M1) is c/2, so one
+//    FP4 -> fp16 conversion gives two values and one packed fp16 fma with
+//    {2d, 2d} and {-2d, -2d} turns them into d*(c-2), exactly (two
+//    instructions per two weights, a mask per eight).
 //  * The contraction runs on v_mfma_f32_32x32x16_f16: a 32-value block is two
 //    MFMAs (the second accumulating onto the first), 16 results per lane.
 //    The activation q (int8) is exact in fp16; a Q2_0 weight d*(c-2) is exact
@@ -34,13 +41,15 @@
 //    the product rounded once, as the oracle rounds it.
 //    (The kernel is bound by VALU issue -- the epilogue FMAs, the weight
 //    decode and the activation staging, four cycles per wave64 instruction --
-//    with the MFMAs partly hidden under that stream; a 16x16x32 form with the
-//    same VALU count per stage measured the same.)
+//    with the MFMAs partly hidden under that stream: at this kernel's ratio
+//    of MFMA to VALU cycles, MFMAs add about 25-30 % to a VALU-only stream in
+//    either shape, 32x32x16 or 16x16x32.)
 //  * MFMA operands: A = weights (lane l: weight row l%32), B = activations
 //    (lane l: activation row l%32); lane half kq = l/32 holds values
 //    16g + 8kq + p (p < 8) of a 32-value block in the MFMA of half g.  Any
 //    assignment that A and B share gives the same exact sum; this one reads
-//    Q2_0 field 2h+g of bytes 8kq..8kq+7 and NL4 nibble g of the same bytes,
+//    the Q2_0 codes of block h from word h of the lane's bytes 8kq..8kq+7
+//    (weight_pack.hip places them there), NL4 nibble g of the same bytes,
 //    and 16 contiguous activation bytes.  A lane's 16 results share one
 //    activation row (one dx per block) and cover weight rows
 //    8q + 4kq + i (q, i < 4), stored as four float4.
@@ -54,8 +63,8 @@
 //    keeps every access inside the expert or the chunk.  The descriptor's
 //    base and range are read from the first lane, which tells the compiler
 //    they are wave-uniform (without that it kept some descriptors in vector
-//    registers and looped over their lanes for every load).  NL4 loads use
-//    clamped 64-bit addresses.
+//    registers and looped over their lanes for every load).  NL4 weights go
+//    through the same descriptors.
 //  * Work lists are grouped per XCD (workgroup id i runs on XCD i % 8): all
 //    chunks of an expert land on one XCD, so its weight tiles and activation
 //    rows are re-read from that XCD's L2.
@@ -111,19 +120,40 @@ __device__ __forceinline__ void i8x4_to_f16(uint32_t w, uint32_t &lo, uint32_t &
     hi = as_u32(as_v2h(perm(0x64646464u, u, 0x07030602u)) + bias);
 }
 
-// Q2_0: field J (the codes of values 16J + b) of the four code bytes in
-// `word`, made into four fp16 weights d*(c-2).  The table {-2d, -d, 0, d}
-// keeps its low bytes in tlo and its high bytes in thi: one byte lookup in
-// each gives the four low and the four high bytes, two byte interleaves give
-// the fp16 pairs.
-template <int J>
-__device__ __forceinline__ void q2_decode4(uint32_t word, uint32_t thi, uint32_t tlo, uint32_t &h01,
-                                           uint32_t &h23) {
-    const uint32_t c = (J == 0 ? word : word >> (2 * J)) & 0x03030303u;
-    const uint32_t lo = perm(0u, tlo, c);
-    const uint32_t hi = perm(0u, thi, c);
-    h01 = perm(hi, lo, 0x05010400u);
-    h23 = perm(hi, lo, 0x07030602u);
+// 4 int8 -> 4 fp16 (two packed pairs), exact, for the LDS staging: one
+// conversion per value, the signed byte picked and packed by the instruction
+// itself.  (Its results only go to LDS: the compiler does not see inside the
+// asm, so it must not feed a matrix-core operand directly.)
+__device__ __forceinline__ void i8x4_to_f16_staged(uint32_t w, uint32_t &lo, uint32_t &hi) {
+    asm("v_cvt_f16_i16_sdwa %0, sext(%2) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0\n\t"
+        "v_cvt_f16_i16_sdwa %0, sext(%2) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1\n\t"
+        "v_cvt_f16_i16_sdwa %1, sext(%2) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_2\n\t"
+        "v_cvt_f16_i16_sdwa %1, sext(%2) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3"
+        : "=&v"(lo), "=&v"(hi)
+        : "v"(w));
+}
+
+// Q2_0 in the tiled layout: byte k of a lane's code word holds two codes in
+// each nibble's low bits (bits 0-1 and 4-5) and two more above them (bits
+// 2-3 and 6-7).  Masked to one pair per byte, a nibble 00cc read as FP4
+// (E2M1) is exactly c/2, so one conversion gives two fp16 values c/2 and one
+// packed fma with {2d, 2d} and {-2d, -2d} gives d*(c-2): the exact product
+// c*d - 2d is a binary16 (|2d| <= 65504), so its single rounding is exact.
+template <int K>
+__device__ __forceinline__ v2h fp4_pair(uint32_t m) {
+    return __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 1.0f, K));
+}
+
+// `word` is the lane's code word of 32-value block h; h[k] gets the fp16
+// weights of values p = 2k, 2k + 1 of the lane's eight in MFMA g.
+template <int G>
+__device__ __forceinline__ void q2_decode8(uint32_t word, uint32_t d2, uint32_t nd2, uint32_t (&h)[4]) {
+    const uint32_t m = (G == 0 ? word : word >> 2) & 0x33333333u;
+    const v2h a = as_v2h(d2), c = as_v2h(nd2);
+    h[0] = as_u32(__builtin_elementwise_fma(fp4_pair<0>(m), a, c));
+    h[1] = as_u32(__builtin_elementwise_fma(fp4_pair<1>(m), a, c));
+    h[2] = as_u32(__builtin_elementwise_fma(fp4_pair<2>(m), a, c));
+    h[3] = as_u32(__builtin_elementwise_fma(fp4_pair<3>(m), a, c));
 }
 
 // NL4: four 4-bit codes (low nibbles of the bytes of c) -> four int8
@@ -167,8 +197,7 @@ template <int WTYPE, int H, int G>
 __device__ __forceinline__ v8h decode_ops(const WRaw &w, uint32_t thi, uint32_t tlo, const uint32_t (&cb)[4]) {
     uint32_t r[4];
     if constexpr (WTYPE == 1) {
-        q2_decode4<2 * H + G>(w.c0.x, thi, tlo, r[0], r[1]);
-        q2_decode4<2 * H + G>(w.c0.y, thi, tlo, r[2], r[3]);
+        q2_decode8<G>(H == 0 ? w.c0.x : w.c0.y, thi, tlo, r);
     } else {
         const uint2 c = H == 0 ? w.c0 : w.c1;
         constexpr int sh = 4 * G;
@@ -178,36 +207,37 @@ __device__ __forceinline__ v8h decode_ops(const WRaw &w, uint32_t thi, uint32_t 
     return pack8(r[0], r[1], r[2], r[3]);
 }
 
-// The fp16 table {-2d, -d, 0, d} of a Q2_0 block scale, split into low and
-// high bytes (code c selects byte c of tlo and byte c of thi).
+// The decode constants of a Q2_0 block scale d: thi = {2d, 2d} (exact: |2d|
+// is at most 65504) and tlo = {-2d, -2d}.
 __device__ __forceinline__ void q2_table(uint32_t hb, uint32_t &thi, uint32_t &tlo) {
     const uint32_t d = hb & 0xFFFFu;
-    // {d, 2d}: the doubling is exact unless it overflows binary16
-    const v2h two = {(_Float16)1.0f, (_Float16)2.0f};
-    const uint32_t pos = as_u32(as_v2h(d | (d << 16)) * two);
-    const uint32_t neg = pos ^ 0x80008000u;                  // {-d, -2d}
-    tlo = perm(neg, pos, 0x000C0406u);
-    thi = perm(neg, pos, 0x010C0507u);
+    const v2h two = {(_Float16)2.0f, (_Float16)2.0f};
+    thi = as_u32(as_v2h(d | (d << 16)) * two);
+    tlo = thi ^ 0x80008000u;
 }
 
-// Quarter i of the staging of one activation block: 8 q bytes to fp16 in LDS.
+// LDS offset of quarter i of a thread's staging: quarters 0-1 are its
+// 16 values of row A, quarters 2-3 the same values of row B (64 rows on).
+constexpr int stage_off(int i) { return i < 2 ? 16 * i : 64 * kARow + 16 * (i - 2); }
+
+// Quarter i of the staging of one thread's activations: 8 q bytes to fp16 in LDS.
 __device__ __forceinline__ void stage_piece(const ARaw &a, int i, uint8_t *dst) {
     const uint32_t q[8] = {a.q0.x, a.q0.y, a.q0.z, a.q0.w, a.q1.x, a.q1.y, a.q1.z, a.q1.w};
     uint4 o;
-    i8x4_to_f16(q[2 * i], o.x, o.y);
-    i8x4_to_f16(q[2 * i + 1], o.z, o.w);
-    *reinterpret_cast<uint4 *>(dst + 16 * i) = o;
+    i8x4_to_f16_staged(q[2 * i], o.x, o.y);
+    i8x4_to_f16_staged(q[2 * i + 1], o.z, o.w);
+    *reinterpret_cast<uint4 *>(dst + stage_off(i)) = o;
 }
 
-// Convert one staged activation block to fp16 and store it in LDS.
+// Convert one thread's staged activations to fp16 and store them in LDS.
 __device__ __forceinline__ void stage_acts(const ARaw &a, uint8_t *dst, float *dx) {
     const uint32_t q[8] = {a.q0.x, a.q0.y, a.q0.z, a.q0.w, a.q1.x, a.q1.y, a.q1.z, a.q1.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         uint4 o;
-        i8x4_to_f16(q[2 * i], o.x, o.y);
-        i8x4_to_f16(q[2 * i + 1], o.z, o.w);
-        *reinterpret_cast<uint4 *>(dst + 16 * i) = o;
+        i8x4_to_f16_staged(q[2 * i], o.x, o.y);
+        i8x4_to_f16_staged(q[2 * i + 1], o.z, o.w);
+        *reinterpret_cast<uint4 *>(dst + stage_off(i)) = o;
     }
     *dx = a.d;
 }
@@ -460,22 +490,29 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
         return w;
     };
 
-    // activations: thread tid stages row tid/2 (clamped), block tid&1 of a stage
-    const int srow = tid >> 1;
-    const int sblk = tid & 1;
+    // activations: thread tid stages values 16p..16p+15 (p = tid&3) of the
+    // stage in rows tid/4 and 64 + tid/4 (clamped), so four lanes read one
+    // row's 64 contiguous bytes; it loads the scale of block p&1 of row
+    // tid/4 (p < 2) or of row 64 + tid/4
+    const int srow = tid >> 2;
+    const int spc = tid & 3;
+    const int drow = srow + 64 * (spc >> 1), dblk = spc & 1;
     const uint8_t *abase = a.act + size_t(row0) * arb;
-    const uint32_t aoff = uint32_t(min(srow, nrows - 1)) * arb;
+    const uint32_t aoffA = uint32_t(min(srow, nrows - 1)) * arb;
+    const uint32_t aoffB = uint32_t(min(srow + 64, nrows - 1)) * arb;
+    const uint32_t aoffD = uint32_t(min(drow, nrows - 1)) * arb;
     // the chunk's rows through one descriptor (past the chunk the range
     // check returns zeros; the block after the last of a row of odd block
     // count reads the row's own scales and sums, staged but never used)
     const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
         (void *)uniform_ptr(abase), 0, __builtin_amdgcn_readfirstlane(int(uint32_t(nrows) * arb)), 0x00020000);
-    const uint32_t aq = aoff + 32u * uint32_t(sblk), ad = aoff + uint32_t(cols) + 4u * uint32_t(sblk);
+    const uint32_t aqA = aoffA + 16u * uint32_t(spc), aqB = aoffB + 16u * uint32_t(spc);
+    const uint32_t ad = aoffD + uint32_t(cols) + 4u * uint32_t(dblk);
     auto aload = [&](int stage) {
         const int s = min(stage, n_stages - 1);
         ARaw r;
-        r.q0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, aq, 64 * s, 0));
-        r.q1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, aq + 16u, 64 * s, 0));
+        r.q0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, aqA, 64 * s, 0));
+        r.q1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, aqB, 64 * s, 0));
         r.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ares, ad, 8 * s, 0));
         return r;
     };
@@ -513,7 +550,7 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
         for (int t = 0; t < 2; ++t) wslot[x][t] = wload(x, t);
         __builtin_amdgcn_sched_barrier(0);
     }
-    stage_acts(aslot[0], &L.act[0][srow * kARow + 64 * sblk], &L.dx[0][srow][sblk]);
+    stage_acts(aslot[0], &L.act[0][srow * kARow + 32 * spc], &L.dx[0][drow][dblk]);
     // the pipelined Q2_0 stage computes the next stage's weight tables itself
     uint32_t pthi[2] = {0u, 0u}, ptlo[2] = {0u, 0u};
     if constexpr (PIPE) {
@@ -536,10 +573,10 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
         if constexpr (PIPE) {
             if (wave_on && s < n_stages)
                 stage_q2_pipelined<NA>(acc, wslot[j], wslot[jn], pthi, ptlo, aslot[jn],
-                                       &L.act[par ^ 1][srow * kARow + 64 * sblk], &L.dx[par ^ 1][srow][sblk],
+                                       &L.act[par ^ 1][srow * kARow + 32 * spc], &L.dx[par ^ 1][drow][dblk],
                                        L.act[par] + col * kARow + 16 * kq, &L.dx[par][col][0]);
             else
-                stage_acts(aslot[jn], &L.act[par ^ 1][srow * kARow + 64 * sblk], &L.dx[par ^ 1][srow][sblk]);
+                stage_acts(aslot[jn], &L.act[par ^ 1][srow * kARow + 32 * spc], &L.dx[par ^ 1][drow][dblk]);
 #pragma unroll
             for (int t = 0; t < 2; ++t) wslot[j][t] = wload(s + U, t);
             __syncthreads();
@@ -618,7 +655,7 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
             });
         }
 
-        stage_acts(aslot[jn], &L.act[par ^ 1][srow * kARow + 64 * sblk], &L.dx[par ^ 1][srow][sblk]);
+        stage_acts(aslot[jn], &L.act[par ^ 1][srow * kARow + 32 * spc], &L.dx[par ^ 1][drow][dblk]);
 #pragma unroll
         for (int t = 0; t < 2; ++t) wslot[j][t] = wload(s + U, t);
         __syncthreads();

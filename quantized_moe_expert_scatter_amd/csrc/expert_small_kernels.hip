@@ -38,10 +38,14 @@ __device__ __forceinline__ float half_to_float(uint32_t bits) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
 }
 
-// Codes of one dword of a Q2_0 block, field j: values 16 j + 4 m .. + 3 as int8 0..3.
-template <int J>
-__device__ __forceinline__ uint32_t q2_field(uint32_t w) {
-    return (w >> (2 * J)) & 0x03030303u;
+// Q2_0 in the tiled layout: for the block's values 32 h + 16 g + 8 kq + p,
+// dword 2 kq + h holds the code of p = 2 k in bits 2 g of byte k and that of
+// p = 2 k + 1 in bits 2 g + 4.  Its codes as int8 0..3, the even p in one
+// dword and the odd p in the other (k = 0..3 in byte k).
+template <int G>
+__device__ __forceinline__ void q2_codes(uint32_t w, uint32_t &even, uint32_t &odd) {
+    even = (G == 0 ? w : w >> 2) & 0x03030303u;
+    odd = (w >> (2 * G + 4)) & 0x03030303u;
 }
 
 // NL4: four 4-bit codes (one per byte) -> four int8 codebook entries.
@@ -128,7 +132,14 @@ __global__ __launch_bounds__(64 * kSmallWaves) void expert_small_kernel(ProductA
         for (int x = 0; x < kPer; ++x) {
             const uint32_t i = uint32_t(tid) + uint32_t(x) * (64 * kSmallWaves);
             const uint32_t r = i / per_row, k = i - r * per_row;
-            if (i < n) *reinterpret_cast<uint2 *>(s_act + r * lstride + 8u * k) = v[x];
+            if (i < n) {
+                uint2 o = v[x];
+                // Q2_0: a group of eight q as its even then its odd values
+                if (WTYPE == 1 && k < uint32_t(cols) / 8u)
+                    o = uint2{__builtin_amdgcn_perm(v[x].y, v[x].x, 0x06040200u),
+                              __builtin_amdgcn_perm(v[x].y, v[x].x, 0x07050301u)};
+                *reinterpret_cast<uint2 *>(s_act + r * lstride + 8u * k) = o;
+            }
         }
     }
     __syncthreads();
@@ -154,19 +165,20 @@ __global__ __launch_bounds__(64 * kSmallWaves) void expert_small_kernel(ProductA
         const float dw = half_to_float(w.s);
         const uint32_t cw[4] = {w.c.x, w.c.y, w.c.z, w.c.w};
         if constexpr (WTYPE == 1) {
-            // fields 0, 1 pair with q8_1 block 2 blk, fields 2, 3 with block 2 blk + 1
-            uint32_t e[4][4];
+            // group (h, g, kq) of eight values: h picks the q8_1 block (2 blk + h)
+            uint32_t e[2][2][2][2];          // [h][g][kq][even, odd]
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                e[0][m] = q2_field<0>(cw[m]);
-                e[1][m] = q2_field<1>(cw[m]);
-                e[2][m] = q2_field<2>(cw[m]);
-                e[3][m] = q2_field<3>(cw[m]);
-            }
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int kq = 0; kq < 2; ++kq) {
+                    q2_codes<0>(cw[2 * kq + h], e[h][0][kq][0], e[h][0][kq][1]);
+                    q2_codes<1>(cw[2 * kq + h], e[h][1][kq][0], e[h][1][kq][1]);
+                }
 #pragma unroll
             for (int i = 0; i < kMaxSmallRows; ++i) {
                 if (i >= nrows) break;
                 const uint8_t *arow = s_act + i * lstride;
+                // the row's q, each group of eight staged as its even then its odd values
                 const uint4 *q = reinterpret_cast<const uint4 *>(arow + 64 * blk);
                 const uint4 q0 = q[0], q1 = q[1], q2 = q[2], q3 = q[3];
                 const uint32_t qv[16] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w,
@@ -176,13 +188,16 @@ __global__ __launch_bounds__(64 * kSmallWaves) void expert_small_kernel(ProductA
                 const int2 sb = *reinterpret_cast<const int2 *>(s_base + i * lstride + 8 * blk);
                 const float2 dxb = *reinterpret_cast<const float2 *>(dx_base + i * lstride + 8 * blk);
                 int d0 = -2 * sb.x, d1 = -2 * sb.y;
+                // group (h, g, kq) is q dwords 2 (4 h + 2 g + kq) (even) and + 1 (odd)
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    d0 = __builtin_amdgcn_sdot4(int(e[0][m]), int(qv[m]), d0, false);
-                    d0 = __builtin_amdgcn_sdot4(int(e[1][m]), int(qv[4 + m]), d0, false);
-                    d1 = __builtin_amdgcn_sdot4(int(e[2][m]), int(qv[8 + m]), d1, false);
-                    d1 = __builtin_amdgcn_sdot4(int(e[3][m]), int(qv[12 + m]), d1, false);
-                }
+                for (int g = 0; g < 2; ++g)
+#pragma unroll
+                    for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+                        for (int eo = 0; eo < 2; ++eo) {
+                            d0 = __builtin_amdgcn_sdot4(int(e[0][g][kq][eo]), int(qv[2 * (2 * g + kq) + eo]), d0, false);
+                            d1 = __builtin_amdgcn_sdot4(int(e[1][g][kq][eo]), int(qv[2 * (4 + 2 * g + kq) + eo]), d1, false);
+                        }
                 if constexpr (MODE == kModeDots) {
                     const int rr = row0 + i - a.dots_row_begin;
                     if (wave_on && wrow < a.out_rows && rr >= 0 && rr < a.dots_n_rows) {

@@ -168,9 +168,10 @@ hipError_t launch_stride_offsets(uint64_t *gu_off, uint64_t gu_first, uint64_t g
 // Packs n_expert matrices of rows x blocks_per_row blocks into the tiled
 // layout; expert e's planes start at src/dst + e * expert_stride.  half > 0:
 // the source rows alternate gate/up (2j gate j, 2j+1 up j, j < half) and the
-// packed rows are in split order.
+// packed rows are in split order.  q2: Q2_0 blocks, whose codes are also
+// rearranged within each block (weight_pack.hip).
 hipError_t launch_weight_pack(const uint8_t *src, uint8_t *dst, uint64_t expert_stride,
-                              int n_expert, int rows, int blocks_per_row, int half,
+                              int n_expert, int rows, int blocks_per_row, int half, bool q2,
                               hipStream_t stream);
 
 }  // namespace moe

@@ -280,6 +280,7 @@ static int moe_weights_pack_impl(const moe_weights *w, void *dst, size_t dst_byt
     auto *out = static_cast<uint8_t *>(dst);
     const int nb = w->cols / block_values(w->type);
     const int half = (w->type & MOE_W_GU_INTERLEAVED) ? w->rows / 2 : 0;
+    const bool q2 = base_type(w->type) == MOE_W_Q2_0;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     // experts at a constant stride go in one launch, others one launch each
     bool uniform = w->n_expert <= 65535;
@@ -288,10 +289,10 @@ static int moe_weights_pack_impl(const moe_weights *w, void *dst, size_t dst_byt
         uniform = w->offset[e] >= w->offset[0] && w->offset[e] - w->offset[0] == uint64_t(e) * stride;
     if (uniform)
         return hip_status(launch_weight_pack(src + w->offset[0], out + w->offset[0], stride,
-                                             stride ? w->n_expert : 1, w->rows, nb, half, s));
+                                             stride ? w->n_expert : 1, w->rows, nb, half, q2, s));
     for (int e = 0; e < w->n_expert; ++e) {
         const hipError_t err =
-            launch_weight_pack(src + w->offset[e], out + w->offset[e], 0, 1, w->rows, nb, half, s);
+            launch_weight_pack(src + w->offset[e], out + w->offset[e], 0, 1, w->rows, nb, half, q2, s);
         if (err != hipSuccess) return MOE_EHIP;
     }
     return MOE_OK;

@@ -18,13 +18,33 @@ namespace moe {
 
 namespace {
 
+// Q2_0 codes of one 64-value block in the kernels' order.  Byte 8 kq + 4 h + k
+// of the packed block holds nibble h of source byte 8 kq + 2 k in its low
+// nibble and nibble h of source byte 8 kq + 2 k + 1 in its high nibble: the
+// values 32 h + 16 g + 8 kq + p (p = 2 k, 2 k + 1) at bits 2 g + 4 (p & 1),
+// so that the product kernel's lane half kq finds the eight values of its
+// MFMA (h, g) in the pairs 00cc of word h's bytes after one mask.
+__device__ __forceinline__ uint4 q2_tiled_block(uint4 c) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int kq = 0; kq < 2; ++kq) {
+        const uint32_t s0 = w[2 * kq], s1 = w[2 * kq + 1];
+        const uint32_t ev = __builtin_amdgcn_perm(s1, s0, 0x06040200u);   // bytes 8kq + 2k
+        const uint32_t od = __builtin_amdgcn_perm(s1, s0, 0x07050301u);   // bytes 8kq + 2k + 1
+        o[2 * kq] = (ev & 0x0F0F0F0Fu) | ((od & 0x0F0F0F0Fu) << 4);
+        o[2 * kq + 1] = ((ev >> 4) & 0x0F0F0F0Fu) | (od & 0xF0F0F0F0u);
+    }
+    return uint4{o[0], o[1], o[2], o[3]};
+}
+
 // One thread per block slot of the packed order: slot d is (tile i, block b,
 // row r) with d = (i * nb + b) * 32 + r, filled from block b of row 32 i + r
 // (of row 2n or 2(n - half) + 1 for packed row n when the source alternates
 // gate and up rows).  Writes are contiguous in d; reads gather 16-byte blocks.
 __global__ __launch_bounds__(256) void weight_pack_kernel(const uint8_t *src, uint8_t *dst,
                                                           uint64_t expert_stride, uint32_t n_blocks,
-                                                          uint32_t nb, uint32_t half) {
+                                                          uint32_t nb, uint32_t half, uint32_t q2) {
     const uint32_t d = blockIdx.x * 256u + threadIdx.x;
     if (d >= n_blocks) return;
     const uint64_t e = uint64_t(blockIdx.y) * expert_stride;
@@ -37,8 +57,9 @@ __global__ __launch_bounds__(256) void weight_pack_kernel(const uint8_t *src, ui
     const uint32_t row = 32u * i + r;
     const uint32_t src_row = half == 0 ? row : (row < half ? 2u * row : 2u * (row - half) + 1u);
     const uint32_t s = src_row * nb + b;
-    *reinterpret_cast<uint4 *>(d_codes + size_t(d) * 16) =
-        *reinterpret_cast<const uint4 *>(s_codes + size_t(s) * 16);
+    uint4 c = *reinterpret_cast<const uint4 *>(s_codes + size_t(s) * 16);
+    if (q2) c = q2_tiled_block(c);
+    *reinterpret_cast<uint4 *>(d_codes + size_t(d) * 16) = c;
     const uint16_t *s_scales = reinterpret_cast<const uint16_t *>(s_codes + size_t(n_blocks) * 16);
     uint16_t *d_scales = reinterpret_cast<uint16_t *>(d_codes + size_t(n_blocks) * 16);
     d_scales[d] = s_scales[s];
@@ -47,13 +68,13 @@ __global__ __launch_bounds__(256) void weight_pack_kernel(const uint8_t *src, ui
 }  // namespace
 
 hipError_t launch_weight_pack(const uint8_t *src, uint8_t *dst, uint64_t expert_stride,
-                              int n_expert, int rows, int blocks_per_row, int half,
+                              int n_expert, int rows, int blocks_per_row, int half, bool q2,
                               hipStream_t stream) {
     const uint32_t n_blocks = uint32_t(rows) * uint32_t(blocks_per_row);
     if (n_blocks == 0 || n_expert <= 0) return hipSuccess;
     const dim3 grid((n_blocks + 255u) / 256u, uint32_t(n_expert)), block(256);
     hipLaunchKernelGGL(weight_pack_kernel, grid, block, 0, stream, src, dst, expert_stride, n_blocks,
-                       uint32_t(blocks_per_row), uint32_t(half));
+                       uint32_t(blocks_per_row), uint32_t(half), uint32_t(q2));
     return hipGetLastError();
 }
 

@@ -3,7 +3,10 @@ permutation of each plane, experts at a constant stride (one launch) or in a
 shuffled slot order with gaps (one launch per expert), Q2_0 and NL4.
 
 The expected bytes are the row-major planes rearranged here with numpy:
-block b of row 32 i + r goes to slot (i * blocks_per_row + b) * 32 + r.
+block b of row 32 i + r goes to slot (i * blocks_per_row + b) * 32 + r, and
+within a Q2_0 block the code of value v = 32 h + 16 g + 8 kq + p (stored at
+bits 2 (v // 16) of byte v % 16) moves to bits 2 g + 4 (p % 2) of byte
+8 kq + 4 h + p // 2.
 """
 import numpy as np
 import pytest
@@ -13,6 +16,16 @@ from quantized_moe_expert_scatter_amd import _lib
 from quantized_moe_expert_scatter_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
+
+
+def _q2_codes_rearranged(codes: np.ndarray) -> np.ndarray:
+    """codes: uint8 [n, 16] Q2_0 code blocks -> the kernels' order within each block."""
+    out = np.zeros_like(codes)
+    for v in range(64):
+        c = (codes[:, v % 16] >> (2 * (v // 16))) & 3
+        h, g, kq, p = v // 32, (v // 16) % 2, (v // 8) % 2, v % 8
+        out[:, 8 * kq + 4 * h + p // 2] |= (c << (2 * g + 4 * (p % 2))).astype(np.uint8)
+    return out
 
 
 def _tiled(plane: np.ndarray, rows: int, nb: int, item: int) -> np.ndarray:
@@ -45,7 +58,10 @@ def test_pack_is_the_tiled_permutation(wtype, rows, cols, E, shuffle):
     for e in range(E):
         o = int(w.offsets[e])
         m = w.expert(e)
-        expect[o:o + 16 * n] = _tiled(m[:16 * n], rows, nb, 16)
+        codes = m[:16 * n]
+        if wtype == wl.Q2_0:
+            codes = _q2_codes_rearranged(codes.reshape(n, 16)).reshape(-1)
+        expect[o:o + 16 * n] = _tiled(codes, rows, nb, 16)
         expect[o + 16 * n:o + 18 * n] = _tiled(m[16 * n:], rows, nb, 2)
     assert np.array_equal(out, expect)
 
