@@ -70,6 +70,7 @@
 //    rows are re-read from that XCD's L2.
 #include "internal.h"
 #include "q8_1.cuh"
+#include "swiglu.cuh"
 
 #include <hip/hip_runtime.h>
 
@@ -343,6 +344,14 @@ constexpr int kOut = 0;     // fp32 outputs
 constexpr int kDots = 1;    // the int32 block dots (test export)
 constexpr int kSwiglu = 2;  // gate/up with swiglu and q8_1 of H in the epilogue
 
+// Four rounded values t[0..3] (binary32 whose truncation toward zero is the
+// q value, in [-127, 127]) converted and packed, value k in byte k.
+__device__ __forceinline__ uint32_t pack_trunc_i8x4(float t0, float t1, float t2, float t3) {
+    const uint32_t lo = perm(uint32_t(int32_t(t1)), uint32_t(int32_t(t0)), 0x0C0C0400u);
+    const uint32_t hi = perm(uint32_t(int32_t(t3)), uint32_t(int32_t(t2)), 0x04000C0Cu);
+    return lo | hi;
+}
+
 // q8_1 of one lane's 16 values of a 32-value block whose other 16 sit in
 // lane ^ 32: d = max|x| / 127 (the fp32 divide), q = x / d rounded half away
 // from zero and clamped to [-127, 127].  x / d is the correctly rounded
@@ -350,9 +359,12 @@ constexpr int kSwiglu = 2;  // gate/up with swiglu and q8_1 of H in the epilogue
 // divide per block), then x * r rounded to binary64 and that to binary32.
 // That is exact because the quotient of two binary32 values is never a
 // binary32 rounding boundary and lies at least 2^-49 of its size away from
-// one, while x * r is within 2^-52 of it.  The rounding adds +-1/2 in
-// binary64 (exact for |y| <= 127) and truncates.  q bytes are packed four to
-// a word, value i of the lane in byte i % 4 of word i / 4.
+// one, while x * r is within 2^-52 of it.  The rounding adds +-0.49999997
+// (the binary32 below 1/2) in binary32 and truncates: for every binary32 y
+// in [-127, 127] that is y rounded half away from zero (checked for all of
+// them), where adding 1/2 itself would round 0.49999997 up to 1.  q bytes
+// are packed four to a word, value i of the lane in byte i % 4 of word
+// i / 4, and s is summed from the packed bytes.
 __device__ __forceinline__ void q8_1_half_block(const float (&x)[16], uint32_t (&w)[4], float &d,
                                                 int32_t &sum) {
     float amax = 0.0f;
@@ -365,20 +377,17 @@ __device__ __forceinline__ void q8_1_half_block(const float (&x)[16], uint32_t (
     for (int k = 0; k < 4; ++k) w[k] = 0u;
     if (d != 0.0f) {
         const double r = 1.0 / static_cast<double>(d);
-        int32_t q[16];
+        float t[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const float y = static_cast<float>(static_cast<double>(x[i]) * r);
             const float yc = __builtin_amdgcn_fmed3f(y, -127.0f, 127.0f);
-            const double half = __builtin_copysign(0.5, static_cast<double>(yc));
-            q[i] = static_cast<int32_t>(static_cast<double>(yc) + half);
-            sum += q[i];
+            t[i] = yc + __builtin_copysignf(0x1.fffffep-2f, yc);
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const uint32_t lo = perm(uint32_t(q[4 * k + 1]), uint32_t(q[4 * k]), 0x0C0C0400u);
-            const uint32_t hi = perm(uint32_t(q[4 * k + 3]), uint32_t(q[4 * k + 2]), 0x04000C0Cu);
-            w[k] = lo | hi;
+            w[k] = pack_trunc_i8x4(t[4 * k], t[4 * k + 1], t[4 * k + 2], t[4 * k + 3]);
+            sum = __builtin_amdgcn_sdot4(int(w[k]), 0x01010101, sum, false);
         }
     }
     sum += __shfl_xor(sum, 32);
@@ -392,8 +401,7 @@ __device__ __forceinline__ void swiglu_store_row(const v16f &g, const v16f &u, u
     float h[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const float e = static_cast<float>(exp(-static_cast<double>(g[i])));
-        h[i] = g[i] / (1.0f + e) * u[i];
+        h[i] = silu_div(static_cast<double>(g[i]), 1.0f + exp_neg_rn32(g[i])) * u[i];
     }
     uint32_t w[4];
     float d;

@@ -18,6 +18,7 @@
 // NL4 codes index the sorted int8 codebook through two byte permutes.
 #include "internal.h"
 #include "q8_1.cuh"
+#include "swiglu.cuh"
 
 #include <hip/hip_runtime.h>
 
@@ -260,8 +261,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void expert_small_kernel(ProductA
             // lanes 0..31 hold gate, 32..63 up of the same j
             const float g = acc[i];
             const float u = __shfl_xor(acc[i], 32);
-            const float e = static_cast<float>(exp(-static_cast<double>(g)));
-            const float h = g / (1.0f + e) * u;
+            const float h = g / (1.0f + exp_neg_rn32(g)) * u;
             float amax = __builtin_fabsf(h);
 #pragma unroll
             for (int s = 1; s < 32; s <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, s));

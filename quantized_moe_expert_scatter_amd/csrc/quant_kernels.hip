@@ -8,6 +8,7 @@
 // first lane of each block.
 #include "internal.h"
 #include "q8_1.cuh"
+#include "swiglu.cuh"
 
 #include <hip/hip_runtime.h>
 
@@ -60,9 +61,8 @@ __global__ __launch_bounds__(256) void quantize_scatter_kernel(const float *__re
 
 // "Strata" PR #3752, swiglu_quant commit: swiglu of each gate/up row and q8_1
 // of each 32-value block of the result in one pass; H never reaches memory.
-// silu(g) = g / (1 + E) in fp32 with IEEE division, E = e^-g rounded once to
-// binary32 from a binary64 exponential, so E is the nearest binary32 value
-// except when e^-g lies within about 2^-29 of a rounding boundary.
+// silu(g) = g / (1 + E) in fp32 with IEEE division, E = e^-g rounded to the
+// nearest binary32 (swiglu.cuh).
 // The blocks of all rows form one flat list (row-major), four lanes per
 // block, sixteen consecutive blocks per wavefront, so no lane idles when
 // n_ff is not a multiple of 512.
@@ -88,8 +88,7 @@ __global__ __launch_bounds__(256) void swiglu_q8_kernel(const float *__restrict_
     float h[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const float e = static_cast<float>(exp(-static_cast<double>(g[i])));
-        const float silu = g[i] / (1.0f + e);
+        const float silu = g[i] / (1.0f + exp_neg_rn32(g[i]));
         h[i] = silu * u[i];
     }
     const Q8Lane q = q8_1_quantize8(h);

@@ -13,12 +13,10 @@
  * scales with exponent uniform in {2^-7, 2^-6, 2^-5} and a uniform 10-bit
  * mantissa (values in [0.0078, 0.0625)).
  *
- * Checks (the parity suite's rule): the q8_1 bytes of X equal the oracle's;
- * the gate/up outputs equal it bit for bit; rows of H whose q8_1 bytes differ
- * (an int8 rounding falling the other way) are at most max(2, R/100); the
- * down product's rows without such a flip reach rel RMS <= 1e-5, the others
- * rel <= 1e-2; the fused gate/up + swiglu launch writes the same H bytes as
- * the two-step form.  Exit status 0 on success.
+ * Checks (the parity suite's rule): the q8_1 bytes of X and of H equal the
+ * oracle's; the gate/up and down outputs equal it bit for bit; the fused
+ * gate/up + swiglu launch writes the same H bytes as the two-step form.
+ * Exit status 0 on success.
  */
 #include <hip/hip_runtime_api.h>
 #include <math.h>
@@ -164,33 +162,14 @@ int main(void) {
     if (memcmp(g, g_ref, sizeof(float) * R * 2 * F)) { fprintf(stderr, "gate/up bits differ\n"); fail = 1; }
     if (memcmp(hq, hq2, hq_bytes)) { fprintf(stderr, "fused and two-step H bytes differ\n"); fail = 1; }
     const size_t hrb = hq_bytes / R;
-    int flips = 0;
-    double num = 0.0, den = 0.0, worst_flip = 0.0;
+    int h_rows = 0, dm_rows = 0;
     for (int r = 0; r < R; ++r) {
-        const int flip = memcmp(hq + hrb * r, hq_ref + hrb * r, hrb) != 0;
-        flips += flip;
-        const float *a = dm + (size_t)perm[r] * H, *b = dms + (size_t)r * H;
-        double rn = 0.0, rd = 0.0;
-        for (int n = 0; n < H; ++n) {
-            const double d = (double)a[n] - (double)b[n];
-            rn += d * d;
-            rd += (double)b[n] * (double)b[n];
-        }
-        if (flip) {
-            const double rel = rd > 0.0 ? sqrt(rn / rd) : sqrt(rn);
-            if (rel > worst_flip) worst_flip = rel;
-        } else {
-            num += rn;
-            den += rd;
-        }
+        h_rows += memcmp(hq + hrb * r, hq_ref + hrb * r, hrb) != 0;
+        dm_rows += memcmp(dm + (size_t)perm[r] * H, dms + (size_t)r * H, sizeof(float) * H) != 0;
     }
-    const double rel_rms = den > 0.0 ? sqrt(num / den) : sqrt(num);
-    const int max_flips = R / 100 > 2 ? R / 100 : 2;
-    printf("rows %d, H flip rows %d, down rel RMS (no flip) %.3e, worst flip row rel %.3e\n", R, flips,
-           rel_rms, worst_flip);
-    if (flips > max_flips) { fprintf(stderr, "too many H flips\n"); fail = 1; }
-    if (rel_rms > 1e-5) { fprintf(stderr, "down product rel RMS above 1e-5\n"); fail = 1; }
-    if (worst_flip > 1e-2) { fprintf(stderr, "flip row rel above 1e-2\n"); fail = 1; }
+    printf("rows %d, rows whose H bytes differ %d, rows whose down outputs differ %d\n", R, h_rows, dm_rows);
+    if (h_rows) { fprintf(stderr, "H bytes differ\n"); fail = 1; }
+    if (dm_rows) { fprintf(stderr, "down product bits differ\n"); fail = 1; }
 
     moe_plan_destroy(plan);
     printf(fail ? "FAIL\n" : "OK\n");
