@@ -685,19 +685,48 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
         }
     } else if constexpr (!DOTS) {
         if (!wave_on) return;
+        // Stores of 16 rows x 64 contiguous bytes.  In the MFMA layout lane l
+        // holds row l%32 of a tile and 4-float pieces 8q + 4kq of it, so a store
+        // would cover 32 rows with 32 bytes each: into rows scattered by the
+        // permutation, a pattern that the memory system takes at half the rate
+        // of 64-byte pieces (measured alone).  One
+        // 16-lane row swap between the registers of pieces q = 2p and 2p + 1
+        // (lanes 16-31 and 48-63 of the first with lanes 0-15 and 32-47 of the
+        // second) leaves rows 0-15 of the tile in the first register and rows
+        // 16-31 in the second, each lane with the piece 16p + 4 (l / 32) +
+        // 8 ((l / 16) % 2) of row l % 16 (+16).  The swaps run with every lane
+        // active; only the stores are masked by the chunk's row count.
+        const int sub = lane & 15;
+        const int cpos = nw + 4 * (lane >> 5) + 8 * ((lane >> 4) & 1);
 #pragma unroll
         for (int r = 0; r < NA; ++r) {
-            const int arow = r * 32 + col;
-            if (arow >= nrows) continue;
-            const int rr = row0 + arow;
-            const size_t orow = a.perm ? size_t(a.perm[rr]) : size_t(rr);
-            float *dst = a.out + orow * a.out_rows + nw + 4 * kq;
+            v4f sw[2][2][2];                     // [t][pair p][rows 0-15, rows 16-31]
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<v4f *>(dst + 32 * t + 8 * q) =
-                        v4f{acc[t][r][4 * q], acc[t][r][4 * q + 1], acc[t][r][4 * q + 2], acc[t][r][4 * q + 3]};
+                for (int p = 0; p < 2; ++p)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float lo = acc[t][r][8 * p + i], hi = acc[t][r][8 * p + 4 + i];
+                        const auto x = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, lo),
+                                                                        __builtin_bit_cast(uint32_t, hi), false, false);
+                        sw[t][p][0][i] = __builtin_bit_cast(float, uint32_t(x[0]));
+                        sw[t][p][1][i] = __builtin_bit_cast(float, uint32_t(x[1]));
+                    }
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int arow = r * 32 + 16 * hf + sub;
+                if (arow < nrows) {
+                    const int rr = row0 + arow;
+                    const size_t orow = a.perm ? size_t(a.perm[rr]) : size_t(rr);
+                    float *dst = a.out + orow * a.out_rows + cpos;
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int p = 0; p < 2; ++p)
+                            *reinterpret_cast<v4f *>(dst + 32 * t + 16 * p) = sw[t][p][hf];
+                }
+            }
         }
     }
 }
