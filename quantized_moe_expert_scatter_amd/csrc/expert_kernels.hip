@@ -230,11 +230,13 @@ __device__ __forceinline__ void stage_piece(const ARaw &a, int i, uint8_t *dst) 
     *reinterpret_cast<uint4 *>(dst + stage_off(i)) = o;
 }
 
-// Convert one thread's staged activations to fp16 and store them in LDS.
+// Convert one thread's staged activations to fp16 and store them in LDS
+// (NQ = 2: row A only, for chunks of at most 64 rows).
+template <int NQ>
 __device__ __forceinline__ void stage_acts(const ARaw &a, uint8_t *dst, float *dx) {
     const uint32_t q[8] = {a.q0.x, a.q0.y, a.q0.z, a.q0.w, a.q1.x, a.q1.y, a.q1.z, a.q1.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NQ; ++i) {
         uint4 o;
         i8x4_to_f16_staged(q[2 * i], o.x, o.y);
         i8x4_to_f16_staged(q[2 * i + 1], o.z, o.w);
@@ -309,12 +311,14 @@ __device__ __forceinline__ void stage_q2_pipelined(v16f (&acc)[2][NA], const WRa
             b1 = *reinterpret_cast<const v8h *>(nsrc + 32);
             dx = dxrow0[nr * 32 * 2 + nh];
         }
-        static_for<0, 4>([&](auto II) {
+        // a chunk of at most 64 rows stages row A only (quarters 0-1)
+        constexpr int NQ = NA > 2 ? 4 : 2;
+        static_for<0, NQ>([&](auto II) {
             constexpr int i = decltype(II)::value;
-            constexpr int at = i * NA + 1 < NP - 1 ? i * NA + 1 : NP - 1;
+            constexpr int at = i * (4 / NQ) * NA + 1 < NP - 1 ? i * (4 / NQ) * NA + 1 : NP - 1;
             if constexpr (at == n) {
                 stage_piece(anext, i, sdst);
-                if constexpr (i == 3) *sdx = anext.d;
+                if constexpr (i == NQ - 1) *sdx = anext.d;
             }
         });
         // the next stage's table of tile t, once block 1 of tile t is decoded
@@ -498,6 +502,8 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
         return w;
     };
 
+    // rows 64-127 are staged only for chunks of more than 64 rows
+    constexpr int NQ = NA > 2 ? 4 : 2;
     // activations: thread tid stages values 16p..16p+15 (p = tid&3) of the
     // stage in rows tid/4 and 64 + tid/4 (clamped), so four lanes read one
     // row's 64 contiguous bytes; it loads the scale of block p&1 of row
@@ -520,7 +526,10 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
         const int s = min(stage, n_stages - 1);
         ARaw r;
         r.q0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, aqA, 64 * s, 0));
-        r.q1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, aqB, 64 * s, 0));
+        if constexpr (NQ == 4)
+            r.q1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ares, aqB, 64 * s, 0));
+        else
+            r.q1 = uint4{0u, 0u, 0u, 0u};
         r.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ares, ad, 8 * s, 0));
         return r;
     };
@@ -558,7 +567,7 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
         for (int t = 0; t < 2; ++t) wslot[x][t] = wload(x, t);
         __builtin_amdgcn_sched_barrier(0);
     }
-    stage_acts(aslot[0], &L.act[0][srow * kARow + 32 * spc], &L.dx[0][drow][dblk]);
+    stage_acts<NQ>(aslot[0], &L.act[0][srow * kARow + 32 * spc], &L.dx[0][drow][dblk]);
     // the pipelined Q2_0 stage computes the next stage's weight tables itself
     uint32_t pthi[2] = {0u, 0u}, ptlo[2] = {0u, 0u};
     if constexpr (PIPE) {
@@ -584,7 +593,7 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
                                        &L.act[par ^ 1][srow * kARow + 32 * spc], &L.dx[par ^ 1][drow][dblk],
                                        L.act[par] + col * kARow + 16 * kq, &L.dx[par][col][0]);
             else
-                stage_acts(aslot[jn], &L.act[par ^ 1][srow * kARow + 32 * spc], &L.dx[par ^ 1][drow][dblk]);
+                stage_acts<NQ>(aslot[jn], &L.act[par ^ 1][srow * kARow + 32 * spc], &L.dx[par ^ 1][drow][dblk]);
 #pragma unroll
             for (int t = 0; t < 2; ++t) wslot[j][t] = wload(s + U, t);
             __syncthreads();
@@ -663,7 +672,7 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
             });
         }
 
-        stage_acts(aslot[jn], &L.act[par ^ 1][srow * kARow + 32 * spc], &L.dx[par ^ 1][drow][dblk]);
+        stage_acts<NQ>(aslot[jn], &L.act[par ^ 1][srow * kARow + 32 * spc], &L.dx[par ^ 1][drow][dblk]);
 #pragma unroll
         for (int t = 0; t < 2; ++t) wslot[j][t] = wload(s + U, t);
         __syncthreads();
