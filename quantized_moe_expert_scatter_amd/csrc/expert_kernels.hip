@@ -553,7 +553,8 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
     // the compute is skipped.  Fewer activation tiles leave registers for a
     // deeper prefetch.
     constexpr bool PIPE = WTYPE == 1 && !DOTS;
-    constexpr int U = NA >= 3 ? 2 : (NA >= 2 ? 4 : 6);
+    // (NL4 with four row tiles: one stage ahead; two would spill)
+    constexpr int U = (WTYPE == 2 && NA == 4) ? 1 : (NA >= 3 ? 2 : (NA >= 2 ? 4 : 6));
     WRaw wslot[U][2];
     ARaw aslot[U];
     // the prologue issues the slots' loads in the loop's own order (the
