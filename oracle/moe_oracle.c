@@ -262,9 +262,10 @@ int orc_block_dots(int wtype, const uint8_t *w_base, const uint64_t *w_off,
  * q8_1 of each 32-value block of the result, in one pass, H never stored.
  * The expression is not printed; our reading is silu(g) * u with
  * silu(g) = g / (1 + e^-g) in fp32, where e^-g is the binary32 value
- * nearest to the exact exponential (computed in binary64 and rounded once;
- * a double rounding can only differ when e^-g lies within about 2^-29 of a
- * binary32 rounding boundary). */
+ * nearest to the exact exponential, computed in binary64 and rounded once
+ * (a double rounding could only differ where e^-g lies within about 2^-29 of
+ * a binary32 rounding boundary; for every binary32 g this C library's result
+ * rounds as an 80-bit exponential does, which the host tests check). */
 float orc_swiglu(float g, float u)
 {
     const float e = (float)exp(-(double)g);
