@@ -41,9 +41,11 @@
 //    the product rounded once, as the oracle rounds it.
 //    (The kernel is bound by VALU issue -- the epilogue FMAs, the weight
 //    decode and the activation staging, four cycles per wave64 instruction --
-//    with the MFMAs partly hidden under that stream: at this kernel's ratio
-//    of MFMA to VALU cycles, MFMAs add about 25-30 % to a VALU-only stream in
-//    either shape, 32x32x16 or 16x16x32.)
+//    with the MFMAs hidden under that stream only if they are spread out: an
+//    MFMA issued while the previous one still runs stalls its wave, so two
+//    issued back to back add about a fifth to a VALU-only stream at this
+//    ratio of MFMA to VALU cycles, and the same MFMAs each followed by about
+//    32 cycles of vector work add a twentieth (two waves per SIMD, measured).)
 //  * MFMA operands: A = weights (lane l: weight row l%32), B = activations
 //    (lane l: activation row l%32); lane half kq = l/32 holds values
 //    16g + 8kq + p (p < 8) of a 32-value block in the MFMA of half g.  Any
@@ -260,17 +262,16 @@ struct Lds {
 };
 
 // One stage (two 32-value blocks h) of Q2_0 outputs, software pipelined as
-// one stream of MFMA pairs n = (h, r, t) (activation tile r, weight tile t):
-// each pair issues its two MFMAs back to back, then the whole epilogue of
-// pair n-1, so the vector ALU works on one result while the matrix unit
-// computes the next, and every FMA reads an MFMA result issued eighteen or
-// more instructions earlier (no hazard wait states); each activation operand
-// is read from LDS right after its last use by the previous row tile; the
-// second block's weights are decoded into the registers of the first as soon
-// as those are dead, inside the stream.  The staging of the next stage's
-// activations (four quarters) and the next stage's weight tables (each
-// tile's once its block 1 is decoded) run inside the stream too, ahead of the
-// pairs' FMAs.  Scheduling barriers keep that order.
+// one stream of MFMA pairs n = (h, r, t) (activation tile r, weight tile t).
+// Pair n's two MFMAs are issued apart, each followed by half of the vector
+// work that overlaps them: the epilogue of pair n-1 (eight FMAs after each
+// MFMA), the next row tile's operands read from LDS as soon as their last
+// reader has issued, a quarter of the next stage's activation staging, the
+// decode of block 1's weights of a tile once its block 0 registers are dead,
+// and the next stage's weight tables.  A matrix-core instruction issued while
+// the previous one still runs stalls its wave until the unit is free; spaced
+// by about 32 cycles of vector work, each one issues at once and the two
+// units stay busy together.  Scheduling barriers keep that order.
 template <int NA>
 __device__ __forceinline__ void stage_q2_pipelined(v16f (&acc)[2][NA], const WRaw (&w)[2], const WRaw (&wn)[2],
                                                    uint32_t (&thi)[2], uint32_t (&tlo)[2], const ARaw &anext,
@@ -299,18 +300,22 @@ __device__ __forceinline__ void stage_q2_pipelined(v16f (&acc)[2][NA], const WRa
         constexpr bool next = t == 1 && (r + 1 < NA || h == 0);
         constexpr int nh = r + 1 < NA ? h : 1, nr = r + 1 < NA ? r + 1 : 0;
         const uint8_t *nsrc = arow0 + nr * 32 * kARow + 64 * nh;
-        // the pair's two MFMAs back to back (the second accumulates onto the
-        // first), the next operands, a quarter of the staging or a table,
-        // then the whole epilogue of the previous pair: its MFMAs issued
-        // eighteen instructions earlier, so the FMAs read finished results
+        // block 1's weights of tile dt: half 0 right after the last pair of
+        // tile dt in block 0, half 1 one pair later
+        constexpr int dec0 = n >= 2 * NA - 2 && n < 2 * NA ? n - (2 * NA - 2) : -1;
+        constexpr int dec1 = n >= 2 * NA - 1 && n < 2 * NA + 1 ? n - (2 * NA - 1) : -1;
+
+        // first half: MFMA 0 of the pair, then the reads of the next row
+        // tile's first operand and scale, staging or a table, 8 FMAs of pair n-1
         v16f p = __builtin_amdgcn_mfma_f32_32x32x16_f16(wop[t][0], b0, v16f{}, 0, 0, 0);
-        p = __builtin_amdgcn_mfma_f32_32x32x16_f16(wop[t][1], b1, p, 0, 0, 0);
+        asm volatile("" ::"v"(p));
+        __builtin_amdgcn_sched_barrier(0);
         const float cdx = dx;
         if constexpr (next) {
             b0 = *reinterpret_cast<const v8h *>(nsrc);
-            b1 = *reinterpret_cast<const v8h *>(nsrc + 32);
             dx = dxrow0[nr * 32 * 2 + nh];
         }
+        if constexpr (dec1 >= 0) wop[dec1][1] = decode_ops<1, 1, 1>(w[dec1], thi[dec1], tlo[dec1], cb);
         // a chunk of at most 64 rows stages row A only (quarters 0-1)
         constexpr int NQ = NA > 2 ? 4 : 2;
         static_for<0, NQ>([&](auto II) {
@@ -325,17 +330,24 @@ __device__ __forceinline__ void stage_q2_pipelined(v16f (&acc)[2][NA], const WRa
         if constexpr (h == 1 && r == 0) q2_table(wn[t].s, thi[t], tlo[t]);
         if constexpr (n > 0) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc[pt][pr][i] = __builtin_fmaf(pdx, prev[i], acc[pt][pr][i]);
+            for (int i = 0; i < 8; ++i) acc[pt][pr][i] = __builtin_fmaf(pdx, prev[i], acc[pt][pr][i]);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, next ? 3 : 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, next ? 2 : 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        // block 1's weights of tile t once block 0's last pair of tile t has issued
-        if constexpr (h == 0 && r == NA - 1) {
-            wop[t][0] = decode_ops<1, 1, 0>(w[t], thi[t], tlo[t], cb);
-            wop[t][1] = decode_ops<1, 1, 1>(w[t], thi[t], tlo[t], cb);
-            __builtin_amdgcn_sched_barrier(0);
+
+        // second half: MFMA 1 (onto MFMA 0), the next second operand, the
+        // other 8 FMAs of pair n-1
+        p = __builtin_amdgcn_mfma_f32_32x32x16_f16(wop[t][1], b1, p, 0, 0, 0);
+        asm volatile("" ::"v"(p));
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (next) b1 = *reinterpret_cast<const v8h *>(nsrc + 32);
+        if constexpr (dec0 >= 0) wop[dec0][0] = decode_ops<1, 1, 0>(w[dec0], thi[dec0], tlo[dec0], cb);
+        if constexpr (n > 0) {
+#pragma unroll
+            for (int i = 8; i < 16; ++i) acc[pt][pr][i] = __builtin_fmaf(pdx, prev[i], acc[pt][pr][i]);
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, next ? 1 : 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
         prev = p;
         pdx = cdx;
     });
