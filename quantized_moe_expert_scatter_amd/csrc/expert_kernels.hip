@@ -265,10 +265,12 @@ struct Lds {
 // one stream of MFMA pairs n = (h, r, t) (activation tile r, weight tile t).
 // Pair n's two MFMAs are issued apart, each followed by half of the vector
 // work that overlaps them: the epilogue of pair n-1 (eight FMAs after each
-// MFMA), the next row tile's operands read from LDS as soon as their last
-// reader has issued, a quarter of the next stage's activation staging, the
-// decode of block 1's weights of a tile once its block 0 registers are dead,
-// and the next stage's weight tables.  A matrix-core instruction issued while
+// MFMA; for the first pair, the previous stage's last pair, carried in
+// prev / pdx), the next row tile's operands read from LDS as soon as their
+// last reader has issued, a quarter of the next stage's activation staging,
+// the decode of weight tile 1's block 0 (under the first pair) and of each
+// tile's block 1 once its block 0 registers are dead, and the next stage's
+// weight tables.  A matrix-core instruction issued while
 // the previous one still runs stalls its wave until the unit is free; spaced
 // by about 32 cycles of vector work, each one issues at once and the two
 // units stay busy together.  Scheduling barriers keep that order.
@@ -276,26 +278,23 @@ template <int NA>
 __device__ __forceinline__ void stage_q2_pipelined(v16f (&acc)[2][NA], const WRaw (&w)[2], const WRaw (&wn)[2],
                                                    uint32_t (&thi)[2], uint32_t (&tlo)[2], const ARaw &anext,
                                                    uint8_t *sdst, float *sdx, const uint8_t *arow0,
-                                                   const float *dxrow0) {
+                                                   const float *dxrow0, v16f &prev, float &pdx) {
     constexpr int NP = 4 * NA;                    // pairs in the stage
     const uint32_t cb[4] = {0u, 0u, 0u, 0u};
-    // operands of the first row tile of block 0, then the decode of block 0
+    // operands of the first row tile of block 0 and tile 0's block-0 weights;
+    // tile 1's are decoded under the first pair
     v8h b0 = *reinterpret_cast<const v8h *>(arow0);
     v8h b1 = *reinterpret_cast<const v8h *>(arow0 + 32);
     float dx = dxrow0[0];
     v8h wop[2][2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        wop[t][0] = decode_ops<1, 0, 0>(w[t], thi[t], tlo[t], cb);
-        wop[t][1] = decode_ops<1, 0, 1>(w[t], thi[t], tlo[t], cb);
-    }
+    wop[0][0] = decode_ops<1, 0, 0>(w[0], thi[0], tlo[0], cb);
+    wop[0][1] = decode_ops<1, 0, 1>(w[0], thi[0], tlo[0], cb);
     __builtin_amdgcn_sched_barrier(0);
-    v16f prev;
-    float pdx = 0.0f;
     static_for<0, NP>([&](auto NN) {
         constexpr int n = decltype(NN)::value;
         constexpr int h = n / (2 * NA), r = (n >> 1) % NA, t = n & 1;
-        constexpr int pr = ((n - 1) >> 1) % NA, pt = (n - 1) & 1;
+        // pair n-1 (for n = 0 the previous stage's last pair, carried in)
+        constexpr int pr = n > 0 ? ((n - 1) >> 1) % NA : NA - 1, pt = n > 0 ? (n - 1) & 1 : 1;
         // the operands that follow this row tile: (h, r+1) or (1, 0)
         constexpr bool next = t == 1 && (r + 1 < NA || h == 0);
         constexpr int nh = r + 1 < NA ? h : 1, nr = r + 1 < NA ? r + 1 : 0;
@@ -316,6 +315,7 @@ __device__ __forceinline__ void stage_q2_pipelined(v16f (&acc)[2][NA], const WRa
             dx = dxrow0[nr * 32 * 2 + nh];
         }
         if constexpr (dec1 >= 0) wop[dec1][1] = decode_ops<1, 1, 1>(w[dec1], thi[dec1], tlo[dec1], cb);
+        if constexpr (n == 0) wop[1][0] = decode_ops<1, 0, 0>(w[1], thi[1], tlo[1], cb);
         // a chunk of at most 64 rows stages row A only (quarters 0-1)
         constexpr int NQ = NA > 2 ? 4 : 2;
         static_for<0, NQ>([&](auto II) {
@@ -328,10 +328,8 @@ __device__ __forceinline__ void stage_q2_pipelined(v16f (&acc)[2][NA], const WRa
         });
         // the next stage's table of tile t, once block 1 of tile t is decoded
         if constexpr (h == 1 && r == 0) q2_table(wn[t].s, thi[t], tlo[t]);
-        if constexpr (n > 0) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[pt][pr][i] = __builtin_fmaf(pdx, prev[i], acc[pt][pr][i]);
-        }
+        for (int i = 0; i < 8; ++i) acc[pt][pr][i] = __builtin_fmaf(pdx, prev[i], acc[pt][pr][i]);
         __builtin_amdgcn_sched_group_barrier(0x100, next ? 2 : 0, 0);
         __builtin_amdgcn_sched_barrier(0);
 
@@ -342,18 +340,16 @@ __device__ __forceinline__ void stage_q2_pipelined(v16f (&acc)[2][NA], const WRa
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (next) b1 = *reinterpret_cast<const v8h *>(nsrc + 32);
         if constexpr (dec0 >= 0) wop[dec0][0] = decode_ops<1, 1, 0>(w[dec0], thi[dec0], tlo[dec0], cb);
-        if constexpr (n > 0) {
+        if constexpr (n == 0) wop[1][1] = decode_ops<1, 0, 1>(w[1], thi[1], tlo[1], cb);
 #pragma unroll
-            for (int i = 8; i < 16; ++i) acc[pt][pr][i] = __builtin_fmaf(pdx, prev[i], acc[pt][pr][i]);
-        }
+        for (int i = 8; i < 16; ++i) acc[pt][pr][i] = __builtin_fmaf(pdx, prev[i], acc[pt][pr][i]);
         __builtin_amdgcn_sched_group_barrier(0x100, next ? 1 : 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         prev = p;
         pdx = cdx;
     });
-    constexpr int lr = NA - 1;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[1][lr][i] = __builtin_fmaf(pdx, prev[i], acc[1][lr][i]);
+    // the stage's last pair is left in prev / pdx for the next stage's first
+    // unit (or the item's end)
 }
 
 constexpr int kOut = 0;     // fp32 outputs
@@ -589,6 +585,14 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
     }
     __syncthreads();
 
+    // the pipelined stage's last MFMA pair, whose epilogue runs under the
+    // next stage's first pair (zero before the first stage: fmaf(0, 0, +0)
+    // leaves the accumulator +0)
+    v16f cprev;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cprev[i] = 0.0f;
+    float cpdx = 0.0f;
+
     auto stage = [&](auto J, int s) {
         constexpr int j = decltype(J)::value;           // s % U
         constexpr int jn = (j + 1) % U;
@@ -604,7 +608,7 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
             if (wave_on && s < n_stages)
                 stage_q2_pipelined<NA>(acc, wslot[j], wslot[jn], pthi, ptlo, aslot[jn],
                                        &L.act[par ^ 1][srow * kARow + 32 * spc], &L.dx[par ^ 1][drow][dblk],
-                                       L.act[par] + col * kARow + 16 * kq, &L.dx[par][col][0]);
+                                       L.act[par] + col * kARow + 16 * kq, &L.dx[par][col][0], cprev, cpdx);
             else
                 stage_acts<NQ>(aslot[jn], &L.act[par ^ 1][srow * kARow + 32 * spc], &L.dx[par ^ 1][drow][dblk]);
 #pragma unroll
@@ -693,6 +697,12 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
 
     for (int s0 = 0; s0 < n_stages; s0 += U)
         static_for<0, U>([&](auto J) { stage(J, s0 + decltype(J)::value); });
+    if constexpr (PIPE) {
+        if (wave_on) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[1][NA - 1][i] = __builtin_fmaf(cpdx, cprev[i], acc[1][NA - 1][i]);
+        }
+    }
 
     if constexpr (MODE == kSwiglu) {
         if (!wave_on) return;
