@@ -28,7 +28,7 @@ namespace {
 
 constexpr int kModeOut = 0, kModeDots = 1, kModeSwiglu = 2;   // as in the product kernel
 constexpr int kSmallWaves = 4;        // 256 weight rows per workgroup, one per lane
-constexpr int kSmallSlots = 8;        // weight blocks loaded ahead
+constexpr int kSmallSlots = 4;        // weight blocks loaded ahead
 
 struct SmallRaw {
     uint4 c;          // the lane's 16 code bytes of one block
@@ -175,10 +175,17 @@ __global__ __launch_bounds__(64 * kSmallWaves) void expert_small_kernel(ProductA
                     q2_codes<0>(cw[2 * kq + h], e[h][0][kq][0], e[h][0][kq][1]);
                     q2_codes<1>(cw[2 * kq + h], e[h][1][kq][0], e[h][1][kq][1]);
                 }
+            uint32_t chain = 0u;
 #pragma unroll
             for (int i = 0; i < kMaxSmallRows; ++i) {
                 if (i >= nrows) break;
-                const uint8_t *arow = s_act + i * lstride;
+                // the row's LDS offset passes through an empty asm that also
+                // takes the previous row's dot: the compiler then cannot read
+                // every row's operands up front, which held eight rows' worth
+                // of registers and halved the waves per SIMD
+                uint32_t roff = uint32_t(i) * lstride;
+                asm volatile("" : "+v"(roff) : "v"(chain));
+                const uint8_t *arow = s_act + roff;
                 // the row's q, each group of eight staged as its even then its odd values
                 const uint4 *q = reinterpret_cast<const uint4 *>(arow + 64 * blk);
                 const uint4 q0 = q[0], q1 = q[1], q2 = q[2], q3 = q[3];
@@ -186,8 +193,8 @@ __global__ __launch_bounds__(64 * kSmallWaves) void expert_small_kernel(ProductA
                                          q2.x, q2.y, q2.z, q2.w, q3.x, q3.y, q3.z, q3.w};
                 // each dot starts from the -2 s of its block, so the chain of
                 // four-wide dots ends at sum (c - 2) q (integer, exact)
-                const int2 sb = *reinterpret_cast<const int2 *>(s_base + i * lstride + 8 * blk);
-                const float2 dxb = *reinterpret_cast<const float2 *>(dx_base + i * lstride + 8 * blk);
+                const int2 sb = *reinterpret_cast<const int2 *>(s_base + roff + 8 * blk);
+                const float2 dxb = *reinterpret_cast<const float2 *>(dx_base + roff + 8 * blk);
                 int d0 = -2 * sb.x, d1 = -2 * sb.y;
                 // group (h, g, kq) is q dwords 2 (4 h + 2 g + kq) (even) and + 1 (odd)
 #pragma unroll
@@ -199,6 +206,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void expert_small_kernel(ProductA
                             d0 = __builtin_amdgcn_sdot4(int(e[0][g][kq][eo]), int(qv[2 * (2 * g + kq) + eo]), d0, false);
                             d1 = __builtin_amdgcn_sdot4(int(e[1][g][kq][eo]), int(qv[2 * (4 + 2 * g + kq) + eo]), d1, false);
                         }
+                chain = uint32_t(d0);
                 if constexpr (MODE == kModeDots) {
                     const int rr = row0 + i - a.dots_row_begin;
                     if (wave_on && wrow < a.out_rows && rr >= 0 && rr < a.dots_n_rows) {
