@@ -270,10 +270,12 @@ struct Lds {
 // last reader has issued, a quarter of the next stage's activation staging,
 // the decode of weight tile 1's block 0 (under the first pair) and of each
 // tile's block 1 once its block 0 registers are dead, and the next stage's
-// weight tables.  A matrix-core instruction issued while
-// the previous one still runs stalls its wave until the unit is free; spaced
-// by about 32 cycles of vector work, each one issues at once and the two
-// units stay busy together.  Scheduling barriers keep that order.
+// weight tables.  A matrix-core instruction issued while the previous one
+// still runs stalls its wave until the unit is free; spaced by about 32
+// cycles of vector work, each one issues at once and the two units stay busy
+// together.  Scheduling barriers keep that order, with an empty volatile asm
+// use of each MFMA result: the MFMA builtins are pure, and without it the
+// compiler sank both MFMAs of a pair past the FMAs and barriers below them.
 template <int NA>
 __device__ __forceinline__ void stage_q2_pipelined(v16f (&acc)[2][NA], const WRaw (&w)[2], const WRaw (&wn)[2],
                                                    uint32_t (&thi)[2], uint32_t (&tlo)[2], const ARaw &anext,
