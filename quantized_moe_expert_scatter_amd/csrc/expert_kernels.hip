@@ -257,7 +257,7 @@ __device__ __forceinline__ void static_for(F &&f) {
 
 struct Lds {
     uint8_t act[2][kMaxRows * kARow];   // staged fp16 activations, double buffered
-    float dx[2][kMaxRows][2];           // their block scales (two blocks per stage)
+    float dx[2][2][kMaxRows];           // their block scales: [buffer][block of the stage][row]
     _Float16 dw[kWaves][2][2][32];      // NL4: block scales of each wave's weight rows
 };
 
@@ -276,18 +276,37 @@ struct Lds {
 // together.  Scheduling barriers keep that order, with an empty volatile asm
 // use of each MFMA result: the MFMA builtins are pure, and without it the
 // compiler sank both MFMAs of a pair past the FMAs and barriers below them.
-template <int NA>
+//
+// QL < 4: the last row tile holds at most 8 QL of the chunk's rows and runs
+// with the operands swapped (activations as A, weights as B; both use the
+// same lane layout), so a lane's 16 results are its weight row against
+// activation rows 8q + 4kq + i (q, i < 4) and only the 4 QL results of the
+// rows q < QL get an epilogue FMA.  Those FMAs take one scale per row, read
+// from LDS per block into dxv[h] (QL float4 per block); the item transposes
+// the tile's accumulators back before its stores.
+template <int NA, int QL>
 __device__ __forceinline__ void stage_q2_pipelined(v16f (&acc)[2][NA], const WRaw (&w)[2], const WRaw (&wn)[2],
                                                    uint32_t (&thi)[2], uint32_t (&tlo)[2], const ARaw &anext,
                                                    uint8_t *sdst, float *sdx, const uint8_t *arow0,
-                                                   const float *dxrow0, v16f &prev, float &pdx) {
+                                                   const float *dxrow0, const float *dxt0, v16f &prev, float &pdx,
+                                                   v4f (&dxv)[2][4]) {
     constexpr int NP = 4 * NA;                    // pairs in the stage
+    constexpr bool TR = QL < 4;                   // row tile NA-1 runs transposed
     const uint32_t cb[4] = {0u, 0u, 0u, 0u};
+    // the scales of the transposed tile's rows for block h
+    auto read_dxv = [&](int h) {
+#pragma unroll
+        for (int q = 0; q < QL; ++q) dxv[h][q] = *reinterpret_cast<const v4f *>(dxt0 + h * kMaxRows + 8 * q);
+    };
     // operands of the first row tile of block 0 and tile 0's block-0 weights;
     // tile 1's are decoded under the first pair
     v8h b0 = *reinterpret_cast<const v8h *>(arow0);
     v8h b1 = *reinterpret_cast<const v8h *>(arow0 + 32);
-    float dx = dxrow0[0];
+    float dx = 0.0f;
+    if constexpr (TR && NA == 1)
+        read_dxv(0);
+    else
+        dx = dxrow0[0];
     v8h wop[2][2];
     wop[0][0] = decode_ops<1, 0, 0>(w[0], thi[0], tlo[0], cb);
     wop[0][1] = decode_ops<1, 0, 1>(w[0], thi[0], tlo[0], cb);
@@ -295,26 +314,37 @@ __device__ __forceinline__ void stage_q2_pipelined(v16f (&acc)[2][NA], const WRa
     static_for<0, NP>([&](auto NN) {
         constexpr int n = decltype(NN)::value;
         constexpr int h = n / (2 * NA), r = (n >> 1) % NA, t = n & 1;
+        constexpr bool tr = TR && r == NA - 1;
         // pair n-1 (for n = 0 the previous stage's last pair, carried in)
         constexpr int pr = n > 0 ? ((n - 1) >> 1) % NA : NA - 1, pt = n > 0 ? (n - 1) & 1 : 1;
+        constexpr int ph = n > 0 ? (n - 1) / (2 * NA) : 1;
+        constexpr bool ptr = TR && pr == NA - 1;
         // the operands that follow this row tile: (h, r+1) or (1, 0)
         constexpr bool next = t == 1 && (r + 1 < NA || h == 0);
         constexpr int nh = r + 1 < NA ? h : 1, nr = r + 1 < NA ? r + 1 : 0;
+        constexpr bool ntr = TR && nr == NA - 1;
         const uint8_t *nsrc = arow0 + nr * 32 * kARow + 64 * nh;
         // block 1's weights of tile dt: half 0 right after the last pair of
         // tile dt in block 0, half 1 one pair later
         constexpr int dec0 = n >= 2 * NA - 2 && n < 2 * NA ? n - (2 * NA - 2) : -1;
         constexpr int dec1 = n >= 2 * NA - 1 && n < 2 * NA + 1 ? n - (2 * NA - 1) : -1;
+        // epilogue FMAs of pair n-1 in each half
+        constexpr int F = ptr ? 2 * QL : 8;
 
         // first half: MFMA 0 of the pair, then the reads of the next row
-        // tile's first operand and scale, staging or a table, 8 FMAs of pair n-1
-        v16f p = __builtin_amdgcn_mfma_f32_32x32x16_f16(wop[t][0], b0, v16f{}, 0, 0, 0);
+        // tile's first operand and scale, staging or a table, the first
+        // half of pair n-1's FMAs
+        v16f p = tr ? __builtin_amdgcn_mfma_f32_32x32x16_f16(b0, wop[t][0], v16f{}, 0, 0, 0)
+                    : __builtin_amdgcn_mfma_f32_32x32x16_f16(wop[t][0], b0, v16f{}, 0, 0, 0);
         asm volatile("" ::"v"(p));
         __builtin_amdgcn_sched_barrier(0);
         const float cdx = dx;
         if constexpr (next) {
             b0 = *reinterpret_cast<const v8h *>(nsrc);
-            dx = dxrow0[nr * 32 * 2 + nh];
+            if constexpr (ntr)
+                read_dxv(nh);
+            else
+                dx = dxrow0[nh * kMaxRows + nr * 32];
         }
         if constexpr (dec1 >= 0) wop[dec1][1] = decode_ops<1, 1, 1>(w[dec1], thi[dec1], tlo[dec1], cb);
         if constexpr (n == 0) wop[1][0] = decode_ops<1, 0, 0>(w[1], thi[1], tlo[1], cb);
@@ -331,27 +361,30 @@ __device__ __forceinline__ void stage_q2_pipelined(v16f (&acc)[2][NA], const WRa
         // the next stage's table of tile t, once block 1 of tile t is decoded
         if constexpr (h == 1 && r == 0) q2_table(wn[t].s, thi[t], tlo[t]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[pt][pr][i] = __builtin_fmaf(pdx, prev[i], acc[pt][pr][i]);
-        __builtin_amdgcn_sched_group_barrier(0x100, next ? 2 : 0, 0);
+        for (int i = 0; i < F; ++i)
+            acc[pt][pr][i] = __builtin_fmaf(ptr ? dxv[ph][i >> 2][i & 3] : pdx, prev[i], acc[pt][pr][i]);
+        __builtin_amdgcn_sched_group_barrier(0x100, next ? (ntr ? 1 + QL : 2) : 0, 0);
         __builtin_amdgcn_sched_barrier(0);
 
         // second half: MFMA 1 (onto MFMA 0), the next second operand, the
-        // other 8 FMAs of pair n-1
-        p = __builtin_amdgcn_mfma_f32_32x32x16_f16(wop[t][1], b1, p, 0, 0, 0);
+        // rest of pair n-1's FMAs
+        p = tr ? __builtin_amdgcn_mfma_f32_32x32x16_f16(b1, wop[t][1], p, 0, 0, 0)
+               : __builtin_amdgcn_mfma_f32_32x32x16_f16(wop[t][1], b1, p, 0, 0, 0);
         asm volatile("" ::"v"(p));
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (next) b1 = *reinterpret_cast<const v8h *>(nsrc + 32);
         if constexpr (dec0 >= 0) wop[dec0][0] = decode_ops<1, 1, 0>(w[dec0], thi[dec0], tlo[dec0], cb);
         if constexpr (n == 0) wop[1][1] = decode_ops<1, 0, 1>(w[1], thi[1], tlo[1], cb);
 #pragma unroll
-        for (int i = 8; i < 16; ++i) acc[pt][pr][i] = __builtin_fmaf(pdx, prev[i], acc[pt][pr][i]);
+        for (int i = F; i < 2 * F; ++i)
+            acc[pt][pr][i] = __builtin_fmaf(ptr ? dxv[ph][i >> 2][i & 3] : pdx, prev[i], acc[pt][pr][i]);
         __builtin_amdgcn_sched_group_barrier(0x100, next ? 1 : 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         prev = p;
         pdx = cdx;
     });
-    // the stage's last pair is left in prev / pdx for the next stage's first
-    // unit (or the item's end)
+    // the stage's last pair is left in prev / pdx (dxv[1] when transposed)
+    // for the next stage's first unit (or the item's end)
 }
 
 constexpr int kOut = 0;     // fp32 outputs
@@ -445,7 +478,9 @@ __device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
 // rows rounded up; rows past the chunk are never stored).  In the fused
 // swiglu mode the item's tile is 128 j's: the wave's tile 0 is gate rows
 // j0..j0+31 and its tile 1 the up rows n_ff+j0..n_ff+j0+31 of the same j's.
-template <int WTYPE, int MODE, int NA>
+// QL < 4 (pipelined Q2_0 only): the last row tile holds at most 8 QL rows and
+// runs transposed (see stage_q2_pipelined).
+template <int WTYPE, int MODE, int NA, int QL>
 __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int expert, int row0,
                                          int nrows, int n0) {
     constexpr bool DOTS = MODE == kDots;
@@ -578,7 +613,7 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
         for (int t = 0; t < 2; ++t) wslot[x][t] = wload(x, t);
         __builtin_amdgcn_sched_barrier(0);
     }
-    stage_acts<NQ>(aslot[0], &L.act[0][srow * kARow + 32 * spc], &L.dx[0][drow][dblk]);
+    stage_acts<NQ>(aslot[0], &L.act[0][srow * kARow + 32 * spc], &L.dx[0][dblk][drow]);
     // the pipelined Q2_0 stage computes the next stage's weight tables itself
     uint32_t pthi[2] = {0u, 0u}, ptlo[2] = {0u, 0u};
     if constexpr (PIPE) {
@@ -594,6 +629,13 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
 #pragma unroll
     for (int i = 0; i < 16; ++i) cprev[i] = 0.0f;
     float cpdx = 0.0f;
+    // the transposed tile's row scales per block (QL < 4); zero like cpdx,
+    // since the first stage's carried FMAs read dxv[1]
+    v4f dxv[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dxv[h][q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
     auto stage = [&](auto J, int s) {
         constexpr int j = decltype(J)::value;           // s % U
@@ -608,11 +650,12 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
 
         if constexpr (PIPE) {
             if (wave_on && s < n_stages)
-                stage_q2_pipelined<NA>(acc, wslot[j], wslot[jn], pthi, ptlo, aslot[jn],
-                                       &L.act[par ^ 1][srow * kARow + 32 * spc], &L.dx[par ^ 1][drow][dblk],
-                                       L.act[par] + col * kARow + 16 * kq, &L.dx[par][col][0], cprev, cpdx);
+                stage_q2_pipelined<NA, QL>(acc, wslot[j], wslot[jn], pthi, ptlo, aslot[jn],
+                                           &L.act[par ^ 1][srow * kARow + 32 * spc], &L.dx[par ^ 1][dblk][drow],
+                                           L.act[par] + col * kARow + 16 * kq, &L.dx[par][0][col],
+                                           &L.dx[par][0][32 * (NA - 1) + 4 * kq], cprev, cpdx, dxv);
             else
-                stage_acts<NQ>(aslot[jn], &L.act[par ^ 1][srow * kARow + 32 * spc], &L.dx[par ^ 1][drow][dblk]);
+                stage_acts<NQ>(aslot[jn], &L.act[par ^ 1][srow * kARow + 32 * spc], &L.dx[par ^ 1][dblk][drow]);
 #pragma unroll
             for (int t = 0; t < 2; ++t) wslot[j][t] = wload(s + U, t);
             __syncthreads();
@@ -658,7 +701,7 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
                         const uint8_t *src = abuf + (r * 32 + col) * kARow + (32 * h + 8 * kq) * 2;
                         const v8h b0 = *reinterpret_cast<const v8h *>(src);
                         const v8h b1 = *reinterpret_cast<const v8h *>(src + 32);
-                        const float dx = L.dx[par][r * 32 + col][h];
+                        const float dx = L.dx[par][h][r * 32 + col];
 #pragma unroll
                         for (int t = 0; t < 2; ++t) {
                             v16f p = __builtin_amdgcn_mfma_f32_32x32x16_f16(wop[t][0], b0, v16f{}, 0, 0, 0);
@@ -691,7 +734,7 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
             });
         }
 
-        stage_acts<NQ>(aslot[jn], &L.act[par ^ 1][srow * kARow + 32 * spc], &L.dx[par ^ 1][drow][dblk]);
+        stage_acts<NQ>(aslot[jn], &L.act[par ^ 1][srow * kARow + 32 * spc], &L.dx[par ^ 1][dblk][drow]);
 #pragma unroll
         for (int t = 0; t < 2; ++t) wslot[j][t] = wload(s + U, t);
         __syncthreads();
@@ -701,9 +744,42 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
         static_for<0, U>([&](auto J) { stage(J, s0 + decltype(J)::value); });
     if constexpr (PIPE) {
         if (wave_on) {
+            if constexpr (QL < 4) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc[1][NA - 1][i] = __builtin_fmaf(cpdx, cprev[i], acc[1][NA - 1][i]);
+                for (int i = 0; i < 4 * QL; ++i)
+                    acc[1][NA - 1][i] = __builtin_fmaf(dxv[1][i >> 2][i & 3], cprev[i], acc[1][NA - 1][i]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[1][NA - 1][i] = __builtin_fmaf(cpdx, cprev[i], acc[1][NA - 1][i]);
+            }
         }
+    }
+    if constexpr (QL < 4) {
+        // The transposed tile back to the MFMA layout the stores take, through
+        // the staging buffers (every wave has passed the loop's last barrier,
+        // so none reads them again): lane l holds weight row l%32 against
+        // activation rows 8q + 4kq + i, and reads back activation row l%32
+        // (clamped: rows past 8 QL are past the chunk, never stored) against
+        // weight rows 8q + 4kq + i.  Each wave uses its own quarter.
+        if (!wave_on) return;
+        constexpr int kTP = 36;              // floats per transposed row (padded)
+        float *tp = reinterpret_cast<float *>(&L.act[0][0]) + wave * (2 * 32 * kTP);
+        static_assert(sizeof(L.act) >= size_t(kWaves) * 2 * 32 * kTP * sizeof(float), "transpose space");
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 4 * QL; ++i)
+                tp[(32 * t + 8 * (i >> 2) + 4 * kq + (i & 3)) * kTP + col] = acc[t][NA - 1][i];
+        __builtin_amdgcn_wave_barrier();
+        const int ar = min(col, 8 * QL - 1);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const v4f v = *reinterpret_cast<const v4f *>(&tp[(32 * t + ar) * kTP + 8 * q + 4 * kq]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[t][NA - 1][4 * q + i] = v[i];
+            }
     }
 
     if constexpr (MODE == kSwiglu) {
@@ -765,6 +841,26 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
     }
 }
 
+// The pipelined Q2_0 items take the rows of their last 32-row tile in steps
+// of 8 (1..4); the others always run whole tiles.
+template <int WTYPE, int MODE, int NA>
+__device__ __forceinline__ void run_item_rows(const ProductArgs &a, Lds &L, int expert, int row0, int nrows,
+                                              int n0) {
+    if constexpr (WTYPE == 1 && MODE != kDots) {
+        const int last = nrows - 32 * (NA - 1);
+        if (last <= 8)
+            run_item<WTYPE, MODE, NA, 1>(a, L, expert, row0, nrows, n0);
+        else if (last <= 16)
+            run_item<WTYPE, MODE, NA, 2>(a, L, expert, row0, nrows, n0);
+        else if (last <= 24)
+            run_item<WTYPE, MODE, NA, 3>(a, L, expert, row0, nrows, n0);
+        else
+            run_item<WTYPE, MODE, NA, 4>(a, L, expert, row0, nrows, n0);
+    } else {
+        run_item<WTYPE, MODE, NA, 4>(a, L, expert, row0, nrows, n0);
+    }
+}
+
 template <int WTYPE, int MODE>
 __global__ __launch_bounds__(256, 2) void expert_product_kernel(ProductArgs a) {
     __shared__ __attribute__((aligned(16))) Lds L;
@@ -784,13 +880,13 @@ __global__ __launch_bounds__(256, 2) void expert_product_kernel(ProductArgs a) {
 
     const int na = (nrows + 31) >> 5;          // 32-row activation tiles: 1..4
     if (na <= 1)
-        run_item<WTYPE, MODE, 1>(a, L, expert, row0, nrows, n0);
+        run_item_rows<WTYPE, MODE, 1>(a, L, expert, row0, nrows, n0);
     else if (na == 2)
-        run_item<WTYPE, MODE, 2>(a, L, expert, row0, nrows, n0);
+        run_item_rows<WTYPE, MODE, 2>(a, L, expert, row0, nrows, n0);
     else if (na == 3)
-        run_item<WTYPE, MODE, 3>(a, L, expert, row0, nrows, n0);
+        run_item_rows<WTYPE, MODE, 3>(a, L, expert, row0, nrows, n0);
     else
-        run_item<WTYPE, MODE, 4>(a, L, expert, row0, nrows, n0);
+        run_item_rows<WTYPE, MODE, 4>(a, L, expert, row0, nrows, n0);
 }
 
 hipError_t launch_expert_product(const ProductArgs &a, hipStream_t stream) {

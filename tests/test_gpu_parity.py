@@ -153,6 +153,38 @@ def test_schedule_invariance(chunk_rows):
     B.close()
 
 
+def test_last_tile_row_steps():
+    """Chunks whose last 32-row tile holds 1, 8, 9, 16, 17, 24, 25 or 32 rows,
+    behind 0-3 full tiles: the product kernel runs such a tile in steps of 8
+    rows (both edges of every step), in the four-launch form and in the fused
+    gate/up.  Every element against the oracle."""
+    counts = [32 * (na - 1) + m for na in range(1, 5) for m in (1, 8, 9, 16, 17, 24, 25, 32)]
+    T = sum(counts)
+    cfg = wl.small_config("row_steps", T, 512, 192, len(counts), 1, seed=31)
+    L = wl.make_layer(cfg)
+    # expert e takes counts[e] tokens, in a seeded token order
+    ids = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
+    L.ids = np.random.default_rng(311).permutation(ids).reshape(T, 1)
+    _say("case row_steps", counts)
+    ref = _oracle_full(L)
+    D = device_layer(L, chunk_rows=128)
+    D.run()
+    torch.cuda.synchronize()
+    assert np.array_equal(D.xq_host(), ref.xq), "q8_1 bytes of X"
+    gu = D.gu_host()
+    assert np.array_equal(gu.view(np.uint32), ref.gu.view(np.uint32)), \
+        f"GU bits: rel RMS {rel_rms(gu, ref.gu):.3e}"
+    check_h_exact(D.hq_host(), ref.hq, cfg.n_ff, "row_steps")
+    check_exact(D.dm_host(), ref.dm, "row_steps")
+    D.hq.fill_(0x5A)
+    D.dm.fill_(float("nan"))
+    D.run_fused()
+    torch.cuda.synchronize()
+    check_h_exact(D.hq_host(), ref.hq, cfg.n_ff, "row_steps fused")
+    check_exact(D.dm_host(), ref.dm, "row_steps fused")
+    D.close()
+
+
 def test_deterministic_and_empty():
     L = _small_layer("ragged")
     D = device_layer(L)
