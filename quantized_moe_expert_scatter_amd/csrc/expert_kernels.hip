@@ -255,10 +255,13 @@ __device__ __forceinline__ void static_for(F &&f) {
     }
 }
 
+constexpr int kTP = 36;                 // floats per row of the transposed tile (padded)
+
 struct Lds {
     uint8_t act[2][kMaxRows * kARow];   // staged fp16 activations, double buffered
     float dx[2][2][kMaxRows];           // their block scales: [buffer][block of the stage][row]
     _Float16 dw[kWaves][2][2][32];      // NL4: block scales of each wave's weight rows
+    float tp[kWaves][2][24][kTP];       // each wave's transposed last row tile (at most 24 rows)
 };
 
 // One stage (two 32-value blocks h) of Q2_0 outputs, software pipelined as
@@ -482,7 +485,7 @@ __device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
 // runs transposed (see stage_q2_pipelined).
 template <int WTYPE, int MODE, int NA, int QL>
 __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int expert, int row0,
-                                         int nrows, int n0) {
+                                         int nrows, int n0, int nt) {
     constexpr bool DOTS = MODE == kDots;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -501,7 +504,10 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
     const uint8_t *wexp = a.w_base + a.w_off[expert];
     const int n_ff = a.out_rows >> 1;
     const int nw = MODE == kSwiglu ? n0 + 32 * wave : n0 + 64 * wave;
-    const bool wave_on = nw < (MODE == kSwiglu ? n_ff : a.out_rows);
+    // weight rows (j's in the fused mode) from one N tile to the next
+    constexpr int tstep = MODE == kSwiglu ? kTileRows / 2 : kTileRows;
+    const int wlimit = MODE == kSwiglu ? n_ff : a.out_rows;
+    bool wave_on = nw < wlimit;
     // first weight row of each of the wave's two tiles
     const int tb[2] = {nw, MODE == kSwiglu ? n_ff + nw : nw + 32};
     uint32_t coff[2], soff[2];
@@ -529,14 +535,20 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
     const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
         (void *)uniform_ptr(wexp), 0, __builtin_amdgcn_readfirstlane(int(codes_bytes + codes_bytes / 8u)),
         0x00020000);
-    auto wload = [&](int stage, int t) {
+    // An item's N tiles are whole tiles of the expert when it has more than
+    // one: tile lt of the item is tile 0's rows moved by lt * tstep, which in
+    // the tiled layout is a uniform byte shift of each plane.
+    const int cshift = tstep * nbw * 16, sshift = tstep * nbw * 2;
+    auto wload = [&](int stage, int t, int lt = 0) {
         const int s = min(stage, n_stages - 1);
         const int blk = s * (kKS / WB);                      // first block of the stage
         WRaw w;
-        w.c0 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(wres, coff[t], blk * 512, 0));
+        w.c0 = __builtin_bit_cast(
+            uint2, __builtin_amdgcn_raw_buffer_load_b64(wres, coff[t], blk * 512 + lt * cshift, 0));
         if constexpr (WTYPE == 1) {
             w.c1 = w.c0;
-            w.s = __builtin_amdgcn_raw_buffer_load_b16(wres, 2u * soff[t], int(codes_bytes) + blk * 64, 0);
+            w.s = __builtin_amdgcn_raw_buffer_load_b16(wres, 2u * soff[t],
+                                                       int(codes_bytes) + blk * 64 + lt * sshift, 0);
         } else {
             const int b1 = min(blk + 1, nbw - 1);            // the next block of the same 32 rows
             w.c1 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(wres, coff[t], b1 * 512, 0));
@@ -599,7 +611,7 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
     // deeper prefetch.
     constexpr bool PIPE = WTYPE == 1 && !DOTS;
     // (NL4 with four row tiles: one stage ahead; two would spill)
-    constexpr int U = (WTYPE == 2 && NA == 4) ? 1 : (NA >= 3 ? 2 : (NA >= 2 ? 4 : 6));
+    constexpr int U = (WTYPE == 2 && NA == 4) ? 1 : (NA >= 3 ? 2 : kStreamU);
     WRaw wslot[U][2];
     ARaw aslot[U];
     // the prologue issues the slots' loads in the loop's own order (the
@@ -637,16 +649,18 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
 #pragma unroll
         for (int q = 0; q < 4; ++q) dxv[h][q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto stage = [&](auto J, int s) {
-        constexpr int j = decltype(J)::value;           // s % U
+    // Stage s of the current tile, its LDS buffer par (the parity of the
+    // stage's index in the item's stream); slot j takes the loads of stage ls
+    // of the item's tile lt, U stages on.
+    auto stage = [&](auto J, int s, int par, int ls, int lt) {
+        constexpr int j = decltype(J)::value;
         constexpr int jn = (j + 1) % U;
-        const int par = s & 1;
         const int k0 = s * kKS;
         const int nv = min(kKS, cols - k0);
         const int nblk = WTYPE == 1 ? 2 : (nv >> 5);
         // slot j's activations were staged at the end of the previous stage
-        // (or before the loop), so it takes the load of stage s + U now
-        aslot[j] = aload(s + U);
+        // (or before the loop), so it takes the load U stages on now
+        aslot[j] = aload(ls);
 
         if constexpr (PIPE) {
             if (wave_on && s < n_stages)
@@ -657,7 +671,7 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
             else
                 stage_acts<NQ>(aslot[jn], &L.act[par ^ 1][srow * kARow + 32 * spc], &L.dx[par ^ 1][dblk][drow]);
 #pragma unroll
-            for (int t = 0; t < 2; ++t) wslot[j][t] = wload(s + U, t);
+            for (int t = 0; t < 2; ++t) wslot[j][t] = wload(ls, t, lt);
             __syncthreads();
             return;
         }
@@ -736,107 +750,154 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
 
         stage_acts<NQ>(aslot[jn], &L.act[par ^ 1][srow * kARow + 32 * spc], &L.dx[par ^ 1][dblk][drow]);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) wslot[j][t] = wload(s + U, t);
+        for (int t = 0; t < 2; ++t) wslot[j][t] = wload(ls, t, lt);
         __syncthreads();
     };
 
-    for (int s0 = 0; s0 < n_stages; s0 += U)
-        static_for<0, U>([&](auto J) { stage(J, s0 + decltype(J)::value); });
-    if constexpr (PIPE) {
-        if (wave_on) {
-            if constexpr (QL < 4) {
-#pragma unroll
-                for (int i = 0; i < 4 * QL; ++i)
-                    acc[1][NA - 1][i] = __builtin_fmaf(dxv[1][i >> 2][i & 3], cprev[i], acc[1][NA - 1][i]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) acc[1][NA - 1][i] = __builtin_fmaf(cpdx, cprev[i], acc[1][NA - 1][i]);
-            }
+    // The item's nt N tiles of the chunk as one stream of stages: the groups
+    // of U stages line up with the tiles (the launch takes nt > 1 only where U
+    // divides the stage count), and the last group of a tile issues the loads
+    // of the next tile's first U stages, so that tile starts with its data in
+    // flight; each tile ends with its epilogue and clears its accumulators.
+    // (only items of at most 64 rows with fp32 outputs stream: in larger
+    // items the prefetch slots would stay live through every tile's epilogue,
+    // beside the larger accumulators, and spill; the fused mode's items are
+    // long enough without)
+    constexpr bool STREAM = PIPE && MODE == kOut && NA <= 2;
+    const int ntt = STREAM ? nt : 1;
+    int gpar = 0;                                        // parity of the stream's stage index
+    for (int ti = 0; ti < ntt; ++ti) {
+        const int nwt = nw + ti * tstep;                 // this wave's first weight row (j) in tile ti
+        wave_on = nwt < wlimit;
+        for (int s0 = 0; s0 < n_stages; s0 += U) {
+            const bool nx = s0 + U >= n_stages && ti + 1 < ntt;
+            const int lb = nx ? s0 + U - n_stages : s0 + U;
+            const int lt = nx ? ti + 1 : ti;
+            static_for<0, U>([&](auto J) {
+                constexpr int jj = decltype(J)::value;
+                stage(J, s0 + jj, (gpar + jj) & 1, lb + jj, lt);
+            });
+            gpar = (gpar + U) & 1;
         }
-    }
-    if constexpr (QL < 4) {
-        // The transposed tile back to the MFMA layout the stores take, through
-        // the staging buffers (every wave has passed the loop's last barrier,
-        // so none reads them again): lane l holds weight row l%32 against
-        // activation rows 8q + 4kq + i, and reads back activation row l%32
-        // (clamped: rows past 8 QL are past the chunk, never stored) against
-        // weight rows 8q + 4kq + i.  Each wave uses its own quarter.
-        if (!wave_on) return;
-        constexpr int kTP = 36;              // floats per transposed row (padded)
-        float *tp = reinterpret_cast<float *>(&L.act[0][0]) + wave * (2 * 32 * kTP);
-        static_assert(sizeof(L.act) >= size_t(kWaves) * 2 * 32 * kTP * sizeof(float), "transpose space");
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int i = 0; i < 4 * QL; ++i)
-                tp[(32 * t + 8 * (i >> 2) + 4 * kq + (i & 3)) * kTP + col] = acc[t][NA - 1][i];
-        __builtin_amdgcn_wave_barrier();
-        const int ar = min(col, 8 * QL - 1);
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const v4f v = *reinterpret_cast<const v4f *>(&tp[(32 * t + ar) * kTP + 8 * q + 4 * kq]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[t][NA - 1][4 * q + i] = v[i];
-            }
-    }
 
-    if constexpr (MODE == kSwiglu) {
-        if (!wave_on) return;
-        const size_t hrb = size_t(n_ff) + size_t(n_ff >> 5) * 8;
+        if constexpr (PIPE) {
+            if (wave_on) {
+                if constexpr (QL < 4) {
 #pragma unroll
-        for (int r = 0; r < NA; ++r) {
-            // lanes l and l ^ 32 hold the two halves of a block and share the
-            // activation row, so they skip rows past the chunk together
-            const int arow = r * 32 + col;
-            if (arow < nrows)
-                swiglu_store_row(acc[0][r], acc[1][r], a.hq + size_t(row0 + arow) * hrb, n_ff, nw, kq);
+                    for (int i = 0; i < 4 * QL; ++i)
+                        acc[1][NA - 1][i] = __builtin_fmaf(dxv[1][i >> 2][i & 3], cprev[i], acc[1][NA - 1][i]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        acc[1][NA - 1][i] = __builtin_fmaf(cpdx, cprev[i], acc[1][NA - 1][i]);
+                }
+            }
         }
-    } else if constexpr (!DOTS) {
-        if (!wave_on) return;
-        // Stores of 16 rows x 64 contiguous bytes.  In the MFMA layout lane l
-        // holds row l%32 of a tile and 4-float pieces 8q + 4kq of it, so a store
-        // would cover 32 rows with 32 bytes each: into rows scattered by the
-        // permutation, a pattern that the memory system takes at half the rate
-        // of 64-byte pieces (measured alone).  One
-        // 16-lane row swap between the registers of pieces q = 2p and 2p + 1
-        // (lanes 16-31 and 48-63 of the first with lanes 0-15 and 32-47 of the
-        // second) leaves rows 0-15 of the tile in the first register and rows
-        // 16-31 in the second, each lane with the piece 16p + 4 (l / 32) +
-        // 8 ((l / 16) % 2) of row l % 16 (+16).  The swaps run with every lane
-        // active; only the stores are masked by the chunk's row count.
-        const int sub = lane & 15;
-        const int cpos = nw + 4 * (lane >> 5) + 8 * ((lane >> 4) & 1);
+        if constexpr (QL < 4) {
+            // The transposed tile back to the MFMA layout the stores take,
+            // through the wave's own LDS area: lane l holds weight row l%32
+            // against activation rows 8q + 4kq + i, and reads back activation
+            // row l%32 (clamped: rows past 8 QL are past the chunk, never
+            // stored) against weight rows 8q + 4kq + i.
+            if (wave_on) {
+                float(&tp)[2][24][kTP] = L.tp[wave];
 #pragma unroll
-        for (int r = 0; r < NA; ++r) {
-            v4f sw[2][2][2];                     // [t][pair p][rows 0-15, rows 16-31]
+                for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+                    for (int i = 0; i < 4 * QL; ++i)
+                        tp[t][8 * (i >> 2) + 4 * kq + (i & 3)][col] = acc[t][NA - 1][i];
+                __builtin_amdgcn_wave_barrier();
+                const int ar = min(col, 8 * QL - 1);
 #pragma unroll
-                for (int p = 0; p < 2; ++p)
+                for (int t = 0; t < 2; ++t)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float lo = acc[t][r][8 * p + i], hi = acc[t][r][8 * p + 4 + i];
-                        const auto x = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, lo),
-                                                                        __builtin_bit_cast(uint32_t, hi), false, false);
-                        sw[t][p][0][i] = __builtin_bit_cast(float, uint32_t(x[0]));
-                        sw[t][p][1][i] = __builtin_bit_cast(float, uint32_t(x[1]));
+                    for (int q = 0; q < 4; ++q) {
+                        const v4f v = *reinterpret_cast<const v4f *>(&tp[t][ar][8 * q + 4 * kq]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[t][NA - 1][4 * q + i] = v[i];
                     }
+                // the next tile's transpose writes this area again
+                __builtin_amdgcn_wave_barrier();
+            }
+        }
+
+        if constexpr (MODE == kSwiglu) {
+            if (wave_on) {
+                const size_t hrb = size_t(n_ff) + size_t(n_ff >> 5) * 8;
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const int arow = r * 32 + 16 * hf + sub;
-                if (arow < nrows) {
-                    const int rr = row0 + arow;
-                    const size_t orow = a.perm ? size_t(a.perm[rr]) : size_t(rr);
-                    float *dst = a.out + orow * a.out_rows + cpos;
+                for (int r = 0; r < NA; ++r) {
+                    // lanes l and l ^ 32 hold the two halves of a block and share
+                    // the activation row, so they skip rows past the chunk together
+                    const int arow = r * 32 + col;
+                    if (arow < nrows)
+                        swiglu_store_row(acc[0][r], acc[1][r], a.hq + size_t(row0 + arow) * hrb, n_ff, nwt, kq);
+                }
+            }
+        } else if constexpr (!DOTS) {
+            if (wave_on) {
+                // Stores of 16 rows x 64 contiguous bytes.  In the MFMA layout
+                // lane l holds row l%32 of a tile and 4-float pieces 8q + 4kq of
+                // it, so a store would cover 32 rows with 32 bytes each: into
+                // rows scattered by the permutation, a pattern that the memory
+                // system takes at half the rate of 64-byte pieces (measured
+                // alone).  One 16-lane row swap between the registers of pieces
+                // q = 2p and 2p + 1 (lanes 16-31 and 48-63 of the first with
+                // lanes 0-15 and 32-47 of the second) leaves rows 0-15 of the
+                // tile in the first register and rows 16-31 in the second, each
+                // lane with the piece 16p + 4 (l / 32) + 8 ((l / 16) % 2) of row
+                // l % 16 (+16).  The swaps run with every lane active; only the
+                // stores are masked by the chunk's row count.
+                const int sub = lane & 15;
+                const int cpos = nwt + 4 * (lane >> 5) + 8 * ((lane >> 4) & 1);
+#pragma unroll
+                for (int r = 0; r < NA; ++r) {
+                    v4f sw[2][2][2];                     // [t][pair p][rows 0-15, rows 16-31]
 #pragma unroll
                     for (int t = 0; t < 2; ++t)
 #pragma unroll
                         for (int p = 0; p < 2; ++p)
-                            *reinterpret_cast<v4f *>(dst + 32 * t + 16 * p) = sw[t][p][hf];
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const float lo = acc[t][r][8 * p + i], hi = acc[t][r][8 * p + 4 + i];
+                                const auto x = __builtin_amdgcn_permlane16_swap(
+                                    __builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi), false,
+                                    false);
+                                sw[t][p][0][i] = __builtin_bit_cast(float, uint32_t(x[0]));
+                                sw[t][p][1][i] = __builtin_bit_cast(float, uint32_t(x[1]));
+                            }
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const int arow = r * 32 + 16 * hf + sub;
+                        if (arow < nrows) {
+                            const int rr = row0 + arow;
+                            const size_t orow = a.perm ? size_t(a.perm[rr]) : size_t(rr);
+                            float *dst = a.out + orow * a.out_rows + cpos;
+#pragma unroll
+                            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                                for (int p = 0; p < 2; ++p)
+                                    *reinterpret_cast<v4f *>(dst + 32 * t + 16 * p) = sw[t][p][hf];
+                        }
+                    }
                 }
             }
+        }
+
+        if (ti + 1 < ntt) {
+            // the next tile starts from zero, and so does its first carried pair
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < NA; ++r)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) acc[t][r][i] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) cprev[i] = 0.0f;
+            cpdx = 0.0f;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) dxv[h][q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
         }
     }
 }
@@ -845,19 +906,19 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
 // of 8 (1..4); the others always run whole tiles.
 template <int WTYPE, int MODE, int NA>
 __device__ __forceinline__ void run_item_rows(const ProductArgs &a, Lds &L, int expert, int row0, int nrows,
-                                              int n0) {
+                                              int n0, int nt) {
     if constexpr (WTYPE == 1 && MODE != kDots) {
         const int last = nrows - 32 * (NA - 1);
         if (last <= 8)
-            run_item<WTYPE, MODE, NA, 1>(a, L, expert, row0, nrows, n0);
+            run_item<WTYPE, MODE, NA, 1>(a, L, expert, row0, nrows, n0, nt);
         else if (last <= 16)
-            run_item<WTYPE, MODE, NA, 2>(a, L, expert, row0, nrows, n0);
+            run_item<WTYPE, MODE, NA, 2>(a, L, expert, row0, nrows, n0, nt);
         else if (last <= 24)
-            run_item<WTYPE, MODE, NA, 3>(a, L, expert, row0, nrows, n0);
+            run_item<WTYPE, MODE, NA, 3>(a, L, expert, row0, nrows, n0, nt);
         else
-            run_item<WTYPE, MODE, NA, 4>(a, L, expert, row0, nrows, n0);
+            run_item<WTYPE, MODE, NA, 4>(a, L, expert, row0, nrows, n0, nt);
     } else {
-        run_item<WTYPE, MODE, NA, 4>(a, L, expert, row0, nrows, n0);
+        run_item<WTYPE, MODE, NA, 4>(a, L, expert, row0, nrows, n0, nt);
     }
 }
 
@@ -865,28 +926,33 @@ template <int WTYPE, int MODE>
 __global__ __launch_bounds__(256, 2) void expert_product_kernel(ProductArgs a) {
     __shared__ __attribute__((aligned(16))) Lds L;
 
-    // work item: (chunk, weight tile) from this XCD's list
+    // work item: a chunk from this XCD's list and a group of a.group
+    // consecutive weight tiles of it (the last group of a chunk may be short)
     const int bid = blockIdx.x;
     const int xcd = bid % kXcds;
     const int j = bid / kXcds;
     const int xcnt = a.xcd[kXcds + xcd];
-    if (j >= xcnt * a.n_tiles) return;
-    const int c = a.xcd[xcd] + j / a.n_tiles;
-    const int tile = j % a.n_tiles;
+    const int grp = a.group > 1 ? a.group : 1;
+    const int per_chunk = (a.n_tiles + grp - 1) / grp;
+    if (j >= xcnt * per_chunk) return;
+    const int c = a.xcd[xcd] + j / per_chunk;
+    const int tile = (j % per_chunk) * grp;
+    const int nt = min(grp, a.n_tiles - tile);
     const int expert = a.chunks[4 * c + 0];
     const int row0 = a.chunks[4 * c + 1];
     const int nrows = a.chunks[4 * c + 2];
     const int n0 = tile * (MODE == kSwiglu ? kTileRows / 2 : kTileRows);
 
     const int na = (nrows + 31) >> 5;          // 32-row activation tiles: 1..4
-    if (na <= 1)
-        run_item_rows<WTYPE, MODE, 1>(a, L, expert, row0, nrows, n0);
-    else if (na == 2)
-        run_item_rows<WTYPE, MODE, 2>(a, L, expert, row0, nrows, n0);
-    else if (na == 3)
-        run_item_rows<WTYPE, MODE, 3>(a, L, expert, row0, nrows, n0);
-    else
-        run_item_rows<WTYPE, MODE, 4>(a, L, expert, row0, nrows, n0);
+    if (na <= 1) {
+        run_item_rows<WTYPE, MODE, 1>(a, L, expert, row0, nrows, n0, nt);
+    } else if (na == 2) {
+        run_item_rows<WTYPE, MODE, 2>(a, L, expert, row0, nrows, n0, nt);
+    } else if (na == 3) {
+        run_item_rows<WTYPE, MODE, 3>(a, L, expert, row0, nrows, n0, 1);
+    } else {
+        run_item_rows<WTYPE, MODE, 4>(a, L, expert, row0, nrows, n0, 1);
+    }
 }
 
 hipError_t launch_expert_product(const ProductArgs &a, hipStream_t stream) {

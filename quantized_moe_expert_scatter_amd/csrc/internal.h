@@ -129,8 +129,20 @@ struct ProductArgs {
     int dots_row_begin;
     int dots_n_rows;
     int small_rows;            // chunks of <= small_rows rows go to the small kernel (0: none)
+    // Weight tiles per work item of the product kernel (0 or 1: one).  More
+    // than one only for Q2_0 fp32 outputs (not the fused mode, not the block
+    // dots), every N tile full (out_rows a multiple of kTileRows), the stage
+    // count a multiple of kStreamStages and every chunk of at most 64 rows;
+    // an item's tiles then run as one stream of stages.
+    int group;
     int8_t codebook[16];
 };
+
+// Stages of prefetch of the product kernel's items of at most 64 rows, and
+// what the stage count must be a multiple of for items of several tiles (it
+// takes every prefetch depth of the Q2_0 items: 5 for these, 2 for larger).
+constexpr int kStreamU = 5;
+constexpr int kStreamStages = 10;
 
 // Launchers (defined in the .hip files).  Return hipSuccess or the launch error.
 hipError_t launch_quantize_scatter(const float *x, int tokens, int hidden, int topk,

@@ -23,6 +23,7 @@ using namespace moe;
 struct moe_plan {
     int tokens = 0, topk = 0, n_expert = 0, chunk_rows = 0, rows = 0;
     int hidden = 0, n_ff = 0;
+    int max_chunk_rows = 0;      // rows of the largest chunk (a bound for device-built plans)
     moe_weights gu{}, dn{};
     std::vector<uint64_t> gu_off, dn_off;
     int8_t gu_codebook[16] = {}, dn_codebook[16] = {};
@@ -115,6 +116,7 @@ PlanPtr new_plan(int tokens, int topk, int n_expert, int chunk_rows, const moe_w
                  const moe_weights *w_down) {
     PlanPtr p(new moe_plan);
     p->tokens = tokens; p->topk = topk; p->n_expert = n_expert; p->chunk_rows = chunk_rows;
+    p->max_chunk_rows = chunk_rows;
     p->rows = tokens * topk; p->hidden = w_gu->cols; p->n_ff = w_gu->rows / 2;
     p->gu = *w_gu; p->dn = *w_down;
     p->gu_off.assign(w_gu->offset, w_gu->offset + n_expert);
@@ -359,6 +361,8 @@ static int moe_prefill_plan_impl(const int32_t *ids, int tokens, int topk, int n
     }
     const std::vector<int> order = expert_order(p->counts);
     p->chunks = chunk_list(order, p->counts, p->offsets, chunk_rows);
+    p->max_chunk_rows = n_expert > 0 ? std::min(chunk_rows, *std::max_element(p->counts.begin(), p->counts.end()))
+                                     : 0;
     p->n_chunks = int(p->chunks.size() / 4);
 
     // XCD work lists: every chunk of an expert goes to one XCD so that its
@@ -528,6 +532,7 @@ static int moe_prefill_plan_device_noalloc_impl(const int32_t *ids_dev, int toke
     // the device's plan object: its fields are set here, its containers stay empty
     moe_plan *p = &g_scratch_plans[dev];
     p->tokens = tokens; p->topk = topk; p->n_expert = n_expert; p->chunk_rows = chunk_rows;
+    p->max_chunk_rows = chunk_rows;
     p->rows = tokens * topk; p->hidden = w_gu->cols; p->n_ff = w_gu->rows / 2;
     p->gu = *w_gu; p->dn = *w_down;
     p->gu.offset = nullptr; p->dn.offset = nullptr;      // on the device only
@@ -663,14 +668,35 @@ static ProductArgs product_args(const moe_plan *p, int product, const void *act)
     return a;
 }
 
+// Weight tiles per product-kernel item.  When every chunk has at most 64
+// rows, an item of the down product (10 stages at n_ff 640) is short and its
+// start (the table reads and first weight loads from HBM, about 4 us) is a
+// large part of it: an item then runs up to kGroupTiles tiles of its chunk as
+// one stream, the next tile's first loads in flight under the current tile's
+// last stages (2,048 tokens: 7 % off the down product).  The stream needs
+// Q2_0 fp32 outputs, whole N tiles and a stage count the prefetch depths
+// divide.  The fused gate/up keeps one tile per item: its items are four
+// times longer, and fewer, longer items balanced worse over the XCDs than the
+// start they save (3-7 % slower).
+static int tile_group(const ProductArgs &a, const moe_plan *p) {
+    constexpr int kGroupTiles = 5;
+    const int n_stages = (a.cols + 63) / 64;
+    if (a.wtype != MOE_W_Q2_0 || a.dots || a.hq || p->max_chunk_rows > 64 || n_stages % kStreamStages != 0 ||
+        a.out_rows % kTileRows != 0 || a.n_tiles < 2)
+        return 1;
+    return std::min(a.n_tiles, kGroupTiles);
+}
+
 // The experts of at most a.small_rows rows go to the small kernel, the others
 // to the product kernel, each over its view of the XCD lists (a.n_tiles set);
 // a launch with no item is skipped.
 static hipError_t launch_products(const moe_plan *p, int product, ProductArgs a, hipStream_t stream) {
     hipError_t e = hipSuccess;
+    a.group = 1;
     a.max_items = int(p->max_small[product] * a.n_tiles);
     if (a.max_items > 0) e = launch_expert_small(a, stream);
-    a.max_items = int(p->max_large[product] * a.n_tiles);
+    a.group = tile_group(a, p);
+    a.max_items = int(p->max_large[product] * ((a.n_tiles + a.group - 1) / a.group));
     if (e == hipSuccess && a.max_items > 0) e = launch_expert_product(a, stream);
     return e;
 }

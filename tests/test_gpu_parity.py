@@ -185,6 +185,39 @@ def test_last_tile_row_steps():
     D.close()
 
 
+def test_tile_streams():
+    """Every chunk at most 64 rows and the layer's own widths (hidden 2560,
+    n_ff 640): the product kernel's items with fp32 outputs (down, and gate/up
+    in the four-launch form) then run several N tiles of their chunk as one
+    stream of stages.  Row counts on both edges of every 8-row step of one and
+    two row tiles; every element against the oracle, in the four-launch form
+    and in the fused one."""
+    counts = [32 * (na - 1) + m for na in (1, 2) for m in (1, 8, 9, 16, 17, 24, 25, 32)]
+    T = sum(counts)
+    cfg = wl.small_config("tile_streams", T, 2560, 640, len(counts), 1, seed=32)
+    L = wl.make_layer(cfg)
+    ids = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
+    L.ids = np.random.default_rng(321).permutation(ids).reshape(T, 1)
+    _say("case tile_streams", counts)
+    ref = _oracle_full(L)
+    D = device_layer(L, chunk_rows=128)
+    D.run()
+    torch.cuda.synchronize()
+    assert np.array_equal(D.xq_host(), ref.xq), "q8_1 bytes of X"
+    gu = D.gu_host()
+    assert np.array_equal(gu.view(np.uint32), ref.gu.view(np.uint32)), \
+        f"GU bits: rel RMS {rel_rms(gu, ref.gu):.3e}"
+    check_h_exact(D.hq_host(), ref.hq, cfg.n_ff, "tile_streams")
+    check_exact(D.dm_host(), ref.dm, "tile_streams")
+    D.hq.fill_(0x5A)
+    D.dm.fill_(float("nan"))
+    D.run_fused()
+    torch.cuda.synchronize()
+    check_h_exact(D.hq_host(), ref.hq, cfg.n_ff, "tile_streams fused")
+    check_exact(D.dm_host(), ref.dm, "tile_streams fused")
+    D.close()
+
+
 def test_deterministic_and_empty():
     L = _small_layer("ragged")
     D = device_layer(L)
