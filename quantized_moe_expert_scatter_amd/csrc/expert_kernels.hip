@@ -55,8 +55,11 @@
 //    and 16 contiguous activation bytes.  A lane's 16 results share one
 //    activation row (one dx per block) and cover weight rows
 //    8q + 4kq + i (q, i < 4), stored as four float4.
-//  * Raw weight and activation bytes are loaded 2-6 stages ahead of their use
-//    (deeper when the chunk has fewer rows and registers allow); every load
+//  * A chunk's last 32-row activation tile runs with the MFMA operands
+//    swapped (activations as A), so its epilogue FMAs cover only the rows of
+//    its 8-row steps; its results are transposed back through LDS at the end.
+//  * Raw weight and activation bytes are loaded 2 stages ahead of their use
+//    (5 for chunks of at most 64 rows, whose registers allow it); every load
 //    is unconditional, so no in-flight register is copied (a copy would make
 //    the compiler wait for every outstanding load).  Q2_0 loads go through
 //    buffer descriptors (one per expert's weights, one per chunk's rows): a
@@ -69,7 +72,10 @@
 //    through the same descriptors.
 //  * Work lists are grouped per XCD (workgroup id i runs on XCD i % 8): all
 //    chunks of an expert land on one XCD, so its weight tiles and activation
-//    rows are re-read from that XCD's L2.
+//    rows are re-read from that XCD's L2.  Where every chunk has at most 64
+//    rows, an item of the fp32-output products takes several N tiles of its
+//    chunk as one stream of stages, so only its first tile waits for the
+//    item's table reads and first weight loads.
 #include "internal.h"
 #include "q8_1.cuh"
 #include "swiglu.cuh"
