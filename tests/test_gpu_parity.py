@@ -218,6 +218,37 @@ def test_tile_streams():
     D.close()
 
 
+@pytest.mark.parametrize("device_plan", [False, True])
+def test_tile_streams_short_groups_and_plans(device_plan):
+    """The streams with 64-row chunks cut from experts of up to 150 rows, a
+    hidden width of seven down-product tiles (items of five tiles and of two)
+    and both the host-built and the device-built plan; every element against
+    the oracle."""
+    counts = [150, 129, 128, 100, 65, 64, 63, 40, 33, 32, 17, 9, 8, 1]
+    T = sum(counts)
+    cfg = wl.small_config("tile_streams_1792", T, 1792, 640, len(counts), 1, seed=33)
+    L = wl.make_layer(cfg)
+    ids = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
+    L.ids = np.random.default_rng(331).permutation(ids).reshape(T, 1)
+    _say("case tile_streams_1792 device_plan", device_plan)
+    ref = _oracle_full(L)
+    D = device_layer(L, chunk_rows=64, device_plan=device_plan)
+    D.run()
+    torch.cuda.synchronize()
+    assert np.array_equal(D.xq_host(), ref.xq), "q8_1 bytes of X"
+    gu = D.gu_host()
+    assert np.array_equal(gu.view(np.uint32), ref.gu.view(np.uint32)), \
+        f"GU bits: rel RMS {rel_rms(gu, ref.gu):.3e}"
+    check_h_exact(D.hq_host(), ref.hq, cfg.n_ff, "tile_streams_1792")
+    check_exact(D.dm_host(), ref.dm, "tile_streams_1792")
+    D.dm.fill_(float("nan"))
+    D.run_fused()
+    torch.cuda.synchronize()
+    check_h_exact(D.hq_host(), ref.hq, cfg.n_ff, "tile_streams_1792 fused")
+    check_exact(D.dm_host(), ref.dm, "tile_streams_1792 fused")
+    D.close()
+
+
 def test_deterministic_and_empty():
     L = _small_layer("ragged")
     D = device_layer(L)
