@@ -557,9 +557,12 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
                                                        int(codes_bytes) + blk * 64 + lt * sshift, 0);
         } else {
             const int b1 = min(blk + 1, nbw - 1);            // the next block of the same 32 rows
-            w.c1 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(wres, coff[t], b1 * 512, 0));
-            w.s = uint32_t(__builtin_amdgcn_raw_buffer_load_b16(wres, 2u * soff[t], int(codes_bytes) + blk * 64, 0)) |
-                  (uint32_t(__builtin_amdgcn_raw_buffer_load_b16(wres, 2u * soff[t], int(codes_bytes) + b1 * 64, 0))
+            w.c1 = __builtin_bit_cast(
+                uint2, __builtin_amdgcn_raw_buffer_load_b64(wres, coff[t], b1 * 512 + lt * cshift, 0));
+            w.s = uint32_t(__builtin_amdgcn_raw_buffer_load_b16(wres, 2u * soff[t],
+                                                                int(codes_bytes) + blk * 64 + lt * sshift, 0)) |
+                  (uint32_t(__builtin_amdgcn_raw_buffer_load_b16(wres, 2u * soff[t],
+                                                                 int(codes_bytes) + b1 * 64 + lt * sshift, 0))
                    << 16);
         }
         return w;
