@@ -621,6 +621,9 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
     constexpr bool PIPE = WTYPE == 1 && !DOTS;
     // (NL4 with four row tiles: one stage ahead; two would spill)
     constexpr int U = (WTYPE == 2 && NA == 4) ? 1 : (NA >= 3 ? 2 : kStreamU);
+    // the pipelined stage computes the next stage's weight tables from the
+    // next slot, which must then hold the next stage (not this one)
+    static_assert(!PIPE || U >= 2, "pipelined Q2_0 stages need two or more prefetch slots");
     WRaw wslot[U][2];
     ARaw aslot[U];
     // the prologue issues the slots' loads in the loop's own order (the
