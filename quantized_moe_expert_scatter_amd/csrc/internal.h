@@ -132,8 +132,9 @@ struct ProductArgs {
     // Weight tiles per work item of the product kernel (0 or 1: one).  More
     // than one only for Q2_0 fp32 outputs (not the fused mode, not the block
     // dots), every N tile full (out_rows a multiple of kTileRows), the stage
-    // count a multiple of kStreamStages and every chunk of at most 64 rows;
-    // an item's tiles then run as one stream of stages.
+    // count a multiple of kStreamStages and every chunk of at most 64 rows
+    // (the launch takes it for short items only); an item's tiles then run as
+    // one stream of stages.
     int group;
     int8_t codebook[16];
 };

@@ -669,20 +669,22 @@ static ProductArgs product_args(const moe_plan *p, int product, const void *act)
 }
 
 // Weight tiles per product-kernel item.  When every chunk has at most 64
-// rows, an item of the down product (10 stages at n_ff 640) is short and its
-// start (the table reads and first weight loads from HBM, about 4 us) is a
-// large part of it: an item then runs up to kGroupTiles tiles of its chunk as
-// one stream, the next tile's first loads in flight under the current tile's
-// last stages (2,048 tokens: 7 % off the down product).  The stream needs
-// Q2_0 fp32 outputs, whole N tiles and a stage count the prefetch depths
-// divide.  The fused gate/up keeps one tile per item: its items are four
-// times longer, and fewer, longer items balanced worse over the XCDs than the
-// start they save (3-7 % slower).
+// rows, an item of at most kShortStages stages (the down product: 10 at
+// n_ff 640) is short and its start (the table reads and first weight loads
+// from HBM, about 4 us) is a large part of it: an item then runs up to
+// kGroupTiles tiles of its chunk as one stream, the next tile's first loads in
+// flight under the current tile's last stages (2,048 tokens: 5-8 % off the
+// down product).  The stream needs Q2_0 fp32 outputs, whole N tiles and a
+// stage count the prefetch depths divide.  Longer items keep one tile each:
+// the gate/up's (40 stages) are four times longer, and fewer, longer items
+// balanced worse over the XCDs than the start they save (fused 3-7 %, and the
+// four-launch form's gate/up 9 %, slower).
 static int tile_group(const ProductArgs &a, const moe_plan *p) {
     constexpr int kGroupTiles = 5;
+    constexpr int kShortStages = 16;
     const int n_stages = (a.cols + 63) / 64;
-    if (a.wtype != MOE_W_Q2_0 || a.dots || a.hq || p->max_chunk_rows > 64 || n_stages % kStreamStages != 0 ||
-        a.out_rows % kTileRows != 0 || a.n_tiles < 2)
+    if (a.wtype != MOE_W_Q2_0 || a.dots || a.hq || p->max_chunk_rows > 64 || n_stages > kShortStages ||
+        n_stages % kStreamStages != 0 || a.out_rows % kTileRows != 0 || a.n_tiles < 2)
         return 1;
     return std::min(a.n_tiles, kGroupTiles);
 }

@@ -187,11 +187,10 @@ def test_last_tile_row_steps():
 
 def test_tile_streams():
     """Every chunk at most 64 rows and the layer's own widths (hidden 2560,
-    n_ff 640): the product kernel's items with fp32 outputs (down, and gate/up
-    in the four-launch form) then run several N tiles of their chunk as one
-    stream of stages.  Row counts on both edges of every 8-row step of one and
-    two row tiles; every element against the oracle, in the four-launch form
-    and in the fused one."""
+    n_ff 640): the down product's items (10 stages) then run several N tiles
+    of their chunk as one stream of stages.  Row counts on both edges of every
+    8-row step of one and two row tiles; every element against the oracle, in
+    the four-launch form and in the fused one."""
     counts = [32 * (na - 1) + m for na in (1, 2) for m in (1, 8, 9, 16, 17, 24, 25, 32)]
     T = sum(counts)
     cfg = wl.small_config("tile_streams", T, 2560, 640, len(counts), 1, seed=32)
