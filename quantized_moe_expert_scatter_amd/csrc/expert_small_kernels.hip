@@ -28,7 +28,10 @@ namespace {
 
 constexpr int kModeOut = 0, kModeDots = 1, kModeSwiglu = 2;   // as in the product kernel
 constexpr int kSmallWaves = 4;        // 256 weight rows per workgroup, one per lane
-constexpr int kSmallSlots = 4;        // weight blocks loaded ahead
+// weight blocks loaded ahead: Q2_0 8 (168 VGPRs, still three waves per
+// SIMD), NL4 4 (eight measured slower)
+template <int WTYPE>
+constexpr int small_slots() { return WTYPE == 1 ? 8 : 4; }
 
 struct SmallRaw {
     uint4 c;          // the lane's 16 code bytes of one block
@@ -111,9 +114,10 @@ __global__ __launch_bounds__(64 * kSmallWaves) void expert_small_kernel(ProductA
         return r;
     };
 
-    SmallRaw slot[kSmallSlots];
+    constexpr int kSlots = small_slots<WTYPE>();
+    SmallRaw slot[kSlots];
 #pragma unroll
-    for (int x = 0; x < kSmallSlots; ++x) slot[x] = wload(x);
+    for (int x = 0; x < kSlots; ++x) slot[x] = wload(x);
 
     // the chunk's q8_1 rows into LDS, 8 bytes at a time (rows are 8-byte
     // aligned): every load of the thread is issued before the first store
@@ -249,13 +253,13 @@ __global__ __launch_bounds__(64 * kSmallWaves) void expert_small_kernel(ProductA
         }
     };
 
-    // the block stream, kSmallSlots ahead; loads past the end are clamped
-    for (int b0 = 0; b0 < nbw; b0 += kSmallSlots) {
+    // the block stream, kSlots ahead; loads past the end are clamped
+    for (int b0 = 0; b0 < nbw; b0 += kSlots) {
 #pragma unroll
-        for (int x = 0; x < kSmallSlots; ++x) {
+        for (int x = 0; x < kSlots; ++x) {
             const int blk = b0 + x;
             if (blk < nbw) block(slot[x], blk);
-            slot[x] = wload(blk + kSmallSlots);
+            slot[x] = wload(blk + kSlots);
         }
     }
 
