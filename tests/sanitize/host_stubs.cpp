@@ -20,7 +20,7 @@ hipError_t launch_device_plan(const int32_t *, int, int, int, int, int, uint8_t 
 hipError_t launch_combine(const float *, const float *, int, int, int, float *, hipStream_t) {
     return hipErrorNotSupported;
 }
-hipError_t launch_weight_pack(const uint8_t *, uint8_t *, uint64_t, int, int, int, int, hipStream_t) {
+hipError_t launch_weight_pack(const uint8_t *, uint8_t *, uint64_t, int, int, int, int, bool, hipStream_t) {
     return hipErrorNotSupported;
 }
 hipError_t scratch_workspace(void **) { return hipErrorNotSupported; }
