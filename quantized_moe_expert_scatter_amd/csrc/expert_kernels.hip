@@ -571,16 +571,20 @@ __device__ __forceinline__ void run_item(const ProductArgs &a, Lds &L, int exper
     // rows 64-127 are staged only for chunks of more than 64 rows
     constexpr int NQ = NA > 2 ? 4 : 2;
     // activations: thread tid stages values 16p..16p+15 (p = tid&3) of the
-    // stage in rows tid/4 and 64 + tid/4 (clamped), so four lanes read one
-    // row's 64 contiguous bytes; it loads the scale of block p&1 of row
-    // tid/4 (p < 2) or of row 64 + tid/4
+    // stage in rows tid/4 and 64 + tid/4, so four lanes read one row's 64
+    // contiguous bytes; it loads the scale of block p&1 of row tid/4 (p < 2)
+    // or of row 64 + tid/4.  Rows past the chunk are not clamped: the
+    // descriptor's range check returns zeros for them, so the padded rows of
+    // the last tile are staged as zeros (the matrix core then multiplies
+    // zeros, which costs less power than copies of a real row, and no load
+    // goes to memory for them; their results are never stored).
     const int srow = tid >> 2;
     const int spc = tid & 3;
     const int drow = srow + 64 * (spc >> 1), dblk = spc & 1;
     const uint8_t *abase = a.act + size_t(row0) * arb;
-    const uint32_t aoffA = uint32_t(min(srow, nrows - 1)) * arb;
-    const uint32_t aoffB = uint32_t(min(srow + 64, nrows - 1)) * arb;
-    const uint32_t aoffD = uint32_t(min(drow, nrows - 1)) * arb;
+    const uint32_t aoffA = uint32_t(srow) * arb;
+    const uint32_t aoffB = uint32_t(srow + 64) * arb;
+    const uint32_t aoffD = uint32_t(drow) * arb;
     // the chunk's rows through one descriptor (past the chunk the range
     // check returns zeros; the block after the last of a row of odd block
     // count reads the row's own scales and sums, staged but never used)
