@@ -67,7 +67,7 @@ def test_counter_records_apply_only_to_their_source(tmp_path, monkeypatch):
 
 def test_layer_bytes_and_roofline_fields():
     """The layer's algorithmic bytes at the 16,384-token shape (every expert
-    touched) are the survey's 5,541.7 MB: per (token, expert) row 28,480 B,
+    touched) are 5,541.7 MB: per (token, expert) row 28,480 B,
     per token 10,240 B, per expert 1,382,400 B of Q2_0 weights; the dominant
     kernel is placed against the int8 matrix-core peak and HBM."""
     import numpy as np
